@@ -1,0 +1,223 @@
+/*
+ * gdnverify.h -- C ABI of libgdnverify: the GDN (Gated DeltaNet) ReplaySSM
+ * ring spec-verify on AMD Instinct MI355X (gfx950).
+ *
+ * The method (replayssm(B)SpecDecode, a walkthrough of SGLang PR #28695;
+ * PR #28695, #33102 and #36821 summaries on prhub):  every state slot keeps a
+ * frozen fp32 checkpoint S[slot] and a ring of the raw records committed since
+ * (raw k, raw v, gate g, beta).  A verify reconstructs the outputs of the whole
+ * draft window from checkpoint + ring history + window in closed form, never
+ * writing a per-draft state; it also copies the window's raw records into the
+ * ring as a side channel.  Rejecting drafts is a cursor move.  Before the ring
+ * can overflow, an exact sequential fold replays the committed records into
+ * the checkpoint.
+ *
+ * Conventions for every entry point
+ *  - All tensor arguments are DEVICE pointers owned by the caller, packed
+ *    row-major in the layouts given below.  The library never allocates,
+ *    frees or synchronises; each call only enqueues kernels on `stream`
+ *    (a hipStream_t, NULL for the legacy default stream) and returns.
+ *  - Return value: GDN_OK (0) once everything is enqueued; a negative
+ *    gdn_status on a host-side argument error, in which case nothing was
+ *    enqueued; GDN_ELAUNCH if the HIP runtime rejected a launch.
+ *  - Device-side there are no errors, only defined behaviour:
+ *      * a row whose slot_idx is < 0 or >= num_slots is a padding row: it reads
+ *        and writes nothing, its output rows are left untouched (the pages'
+ *        NULL_BLOCK_ID rows, replayssm(B)SpecDecode App. A.1; PR #36821 summary:
+ *        no writes through negative slots);
+ *      * accept counts are clamped to [0, T];
+ *      * write_pos is clamped to [0, L-T] wherever it is read, which never
+ *        binds while the early-flush invariant holds (replayssm(B)SpecDecode
+ *        §8.2);
+ *      * the slots of the non-padding rows of one call must be distinct.
+ *  - Activations (q, k, v, a, b, o and the ring's rawk/rawv) are in the dtype
+ *    `act` of the shape; S, snapshots and the ring's g/beta are fp32;
+ *    indices and cursors are int32.
+ *
+ * Layouts (token index = row * T + t; GQA: value head hv reads qk-head
+ * hv / (HV/H), replayssm(B)SpecDecode App. A.1 parameter table):
+ *    q, k       [B*T, H, K]            v, o   [B*T, HV, V]
+ *    a, b       [B*T, HV]              A_log, dt_bias [HV] fp32
+ *    S          [num_slots, HV, V, K]  fp32 checkpoint, K contiguous
+ *    ring_rawk  [num_slots, H, L, K]   ring_rawv [num_slots, HV, L, V]
+ *    ring_g     [num_slots, HV, L]     ring_beta [num_slots, HV, L]   fp32
+ *    write_pos, cache_base, is_flush   [num_slots] int32, shared by all layers
+ *    slot_idx   [B] int32              snap [B, T, HV, V, K] fp32
+ *  Record j of a slot's committed history is at physical ring position
+ *  (cache_base + j) & (L-1) (replayssm(B)SpecDecode §10.1).
+ */
+#ifndef GDNVERIFY_H
+#define GDNVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,        /* malformed shape, null or misaligned pointer   */
+    GDN_EUNSUPPORTED = -2,  /* well-formed but outside what the kernels cover */
+    GDN_ELAUNCH = -3        /* the HIP runtime refused a kernel launch        */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/*
+ * Geometry of one GDN layer's verify.  Host-side validation (mirrors the
+ * pages' configuration checks: PR #28695 summary, server_args snippet: ring
+ * length at least twice the draft count; PR #36821 summary, ring view checks):
+ *   B >= 0; 1 <= T <= max_spec_len <= 16; L a power of two, 2*max_spec_len <= L
+ *   <= 128; H >= 1; HV % H == 0; K in {64, 128, 256}; V % 16 == 0, 16 <= V <= 256;
+ *   num_slots >= 1; act in {GDN_F32, GDN_BF16}; l2norm_eps >= 0, finite scale.
+ * Anything else returns GDN_EINVAL (malformed) or GDN_EUNSUPPORTED.
+ */
+typedef struct gdn_shape {
+    int32_t B, T, H, HV, K, V;
+    int32_t L, max_spec_len, num_slots;
+    int32_t act;                 /* gdn_dtype */
+    float scale;                 /* output scale; 1.0 when unused            */
+    float softplus_threshold;    /* softplus(x) = x above it; 20.0 typical   */
+    float l2norm_eps;            /* q/k l2 norm: x / sqrt(sum x^2 + eps)     */
+} gdn_shape;
+
+/*
+ * gdn_spec_verify_ring -- the verify step of one layer
+ * (replayssm(B)SpecDecode §1.1, §4.1, §5.1, §9.1; PR #33102 report anchor 1;
+ *  PR #36821 summary implementation item 1).
+ *
+ * For every non-padding row b with slot s = slot_idx[b] and value head hv:
+ *   hist = is_flush[s] ? 0 : write_pos[s];
+ *   S_c  = S[s,hv] stepped through the hist committed ring records;
+ *   o[b*T+t, hv, :] = scale * S_t q_hat_t for t = 0..T-1, where S_t is S_c
+ *   stepped through window tokens 0..t with g = -exp(A_log) softplus(a+dt_bias),
+ *   beta = sigmoid(b) and l2-normalised q, k.  Every window position gets an
+ *   output, later-rejected ones included.  The window states are never stored:
+ *   the kernel evaluates the chunked closed form (I+A)^-1 over history+window
+ *   from the frozen checkpoint.
+ * fold_flagged = 1: rows whose slot has is_flush set first get their
+ *   checkpoint S[s] advanced in place by the exact fold of their write_pos
+ *   committed records (the two-launch verify-or-flush routing, §8.1, §9.1);
+ *   fold_flagged = 0: the caller has already folded flagged rows (for example
+ *   with gdn_exact_fold); they are verified with an empty history.  A flagged
+ *   row must be folded exactly once per step.
+ * write_ring = 1: the window's records are written, pre-mutation, at logical
+ *   positions write_pos + t: ring_rawk[s, h, p, :] = k bits (once per qk-head),
+ *   ring_rawv[s, hv, p, :] = v bits, ring_g/ring_beta[s, hv, p] = the fp32 gate
+ *   and beta used by the kernel.  Nothing else in the ring is written and the
+ *   outputs are bitwise identical with write_ring = 0.
+ * S is never written for unflagged rows; cursors are never written.
+ * o must not alias any input.  With write_ring = 0 the ring pointers may be
+ * NULL only if no row is flagged or fold_flagged = 0 and hist reads nothing
+ * (they are always read for history); pass them whenever any history exists.
+ */
+int gdn_spec_verify_ring(const gdn_shape *shape,
+                         const void *q, const void *k, const void *v,
+                         const void *a, const void *b,
+                         const float *A_log, const float *dt_bias,
+                         float *S, const int32_t *slot_idx,
+                         const int32_t *write_pos, const int32_t *cache_base,
+                         const int32_t *is_flush,
+                         void *ring_rawk, void *ring_rawv,
+                         float *ring_g, float *ring_beta,
+                         int write_ring, int fold_flagged,
+                         void *o, void *stream);
+
+/*
+ * gdn_exact_fold -- closed-loop exact fold of committed ring records into the
+ * checkpoint (PR #28695 summary, implementation item 3: sequential replay from
+ * the raw inputs, consistent with the recurrent update; replayssm(B)SpecDecode
+ * §12.7).  For each non-padding row (only those whose slot has is_flush set
+ * when only_flagged = 1) and every value head:
+ *   for j in 0..write_pos-1:  S[s,hv] <- step(S[s,hv], record at
+ *   (cache_base + j) & (L-1)), in place.
+ * The step reads rawk/rawv/g/beta exactly as recorded, normalises the key
+ * with l2norm_eps and uses the same arithmetic as gdn_recurrent_verify_snapshot,
+ * so folding a ring written by a verify reproduces the snapshot path's state
+ * bit for bit.  Cursors are not modified: a row folded while unflagged must
+ * have its cursors rebased (e.g. gdn_reset_cursors) before its next verify.
+ * num_layers >= 1 folds that many layers in one launch; S and the four ring
+ * arrays then hold the layers back to back ([num_layers, ...] of the
+ * per-layer layouts); cursors are shared by all layers.  shape->T is the
+ * draft window of the verifies that wrote the ring (for the write_pos clamp);
+ * q/k/v/a/b are not read.
+ */
+int gdn_exact_fold(const gdn_shape *shape, int num_layers,
+                   float *S, const void *ring_rawk, const void *ring_rawv,
+                   const float *ring_g, const float *ring_beta,
+                   const int32_t *slot_idx, const int32_t *write_pos,
+                   const int32_t *cache_base, const int32_t *is_flush,
+                   int only_flagged, void *stream);
+
+/*
+ * gdn_advance_cursors -- commit by accept count (replayssm(B)SpecDecode §4.2,
+ * §8.1-8.2, §9.3).  For each non-padding row with slot s and a = clamp(accept):
+ *   if is_flush[s]: cache_base[s] = (cache_base[s] + write_pos[s]) & (L-1);
+ *                   write_pos[s] = a
+ *   else:           write_pos[s] += a
+ *   is_flush[s] = (write_pos[s] + 2 * max_spec_len > L)      (strict)
+ * One thread per row; called once per step after sampling.
+ */
+int gdn_advance_cursors(const gdn_shape *shape, const int32_t *slot_idx,
+                        const int32_t *accept, int32_t *write_pos,
+                        int32_t *cache_base, int32_t *is_flush, void *stream);
+
+/*
+ * gdn_reset_cursors -- prefill-to-decode handoff (replayssm(B)SpecDecode
+ * App. A.2): write_pos = 0, cache_base = 0, is_flush = init_flush for the n
+ * listed slots (entries outside [0, num_slots) are skipped).  n >= 0.
+ */
+int gdn_reset_cursors(const gdn_shape *shape, const int32_t *slots, int32_t n,
+                      int32_t init_flush, int32_t *write_pos, int32_t *cache_base,
+                      int32_t *is_flush, void *stream);
+
+/*
+ * gdn_recurrent_verify_snapshot -- the baseline the ring replaces
+ * (PR #28695 summary, gdn_backend snippet: the recurrent target_verify with an
+ * intermediate state buffer; PR #36821 summary: a full [K,V] fp32 snapshot per
+ * head-step).  From S[slot] (read only, no ring history), step through the
+ * window writing snap[b, t, hv] = S_t and o as in gdn_spec_verify_ring.
+ * write_ring = 1 additionally records the window in the ring exactly as the
+ * ring verify does (same positions, same g/beta bits); the ring and cursor
+ * pointers may be NULL when write_ring = 0.  snap must not alias S.
+ */
+int gdn_recurrent_verify_snapshot(const gdn_shape *shape,
+                                  const void *q, const void *k, const void *v,
+                                  const void *a, const void *b,
+                                  const float *A_log, const float *dt_bias,
+                                  const float *S, const int32_t *slot_idx,
+                                  float *snap, void *o,
+                                  void *ring_rawk, void *ring_rawv,
+                                  float *ring_g, float *ring_beta,
+                                  const int32_t *write_pos, const int32_t *cache_base,
+                                  int write_ring, void *stream);
+
+/*
+ * gdn_snapshot_commit -- the baseline's commit: S[slot_idx[b]] =
+ * snap[b, a-1] for rows with a = clamp(accept[b]) >= 1; rows accepting nothing
+ * keep their state (PR #28695 summary: the recurrent path copies the accepted
+ * intermediate state at commit).
+ */
+int gdn_snapshot_commit(const gdn_shape *shape, const float *snap,
+                        const int32_t *slot_idx, const int32_t *accept, float *S,
+                        void *stream);
+
+/* Footprints in bytes (host only, no device work): the per-layer ring
+ * (num_slots * L records) and the per-layer snapshot buffer (B*T*HV*V*K fp32).
+ * 0 for an invalid shape. */
+size_t gdn_ring_bytes(const gdn_shape *shape);
+size_t gdn_snapshot_bytes(const gdn_shape *shape);
+
+/* Host-side check of a shape alone; returns a gdn_status. */
+int gdn_validate_shape(const gdn_shape *shape);
+
+/* Static description of a status code. */
+const char *gdn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDNVERIFY_H */

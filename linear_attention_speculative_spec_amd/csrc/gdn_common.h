@@ -1,0 +1,173 @@
+// gdn_common.h -- device helpers shared by the libgdnverify kernels (gfx950).
+//
+// Everything numeric that two kernels must reproduce bit for bit lives here
+// once: the gating of a window token, the l2 norm and the gated delta step of
+// one state row.  The ring verify and the snapshot verify both call gdn_gate,
+// so the gate/beta they record in the ring are the same bits; the exact fold
+// and the snapshot verify both call rnorm16/step_row, so folding a recorded
+// window reproduces the snapshot path's state exactly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdnverify.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ bf16 helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u)
+{
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// Round-to-nearest-even of two floats into packed bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x)
+{
+    return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+// Activation dtype traits: storage type and exact widening to fp32.
+struct ActF32 {
+    typedef float storage;
+    static constexpr int bytes = 4;
+    __device__ static float load(const storage* p) { return *p; }
+    __device__ static storage from_f32(float x) { return x; }
+};
+
+struct ActBF16 {
+    typedef uint16_t storage;
+    static constexpr int bytes = 2;
+    __device__ static float load(const storage* p) { return bf16_to_f32(*p); }
+    __device__ static storage from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Four consecutive activations widened to fp32 (8-byte or 16-byte load).
+template <class Act>
+__device__ __forceinline__ f32x4 load4(const typename Act::storage* p);
+
+template <>
+__device__ __forceinline__ f32x4 load4<ActF32>(const float* p)
+{
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
+template <>
+__device__ __forceinline__ f32x4 load4<ActBF16>(const uint16_t* p)
+{
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+}
+
+// Raw copy of four activations (the ring's bit-exact side channel).
+template <class Act>
+__device__ __forceinline__ void copy4(typename Act::storage* dst, const typename Act::storage* src)
+{
+    if constexpr (Act::bytes == 4)
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    else
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+}
+
+// ------------------------------------------------------------------ gating
+
+// g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b), in fp32
+// (fused GDN gating with an fp32 sigmoid; softplus is the identity above the
+// threshold).  The one routine every kernel uses for window tokens.
+__device__ __forceinline__ void gdn_gate(float a, float b, float A_log, float dt_bias,
+                                         float threshold, float& g, float& beta)
+{
+    const float x = a + dt_bias;
+    const float sp = x > threshold ? x : log1pf(expf(x));
+    g = -expf(A_log) * sp;
+    beta = 1.0f / (1.0f + expf(-b));
+}
+
+// -------------------------------------------------------- wave reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group receives
+// the same bits (each stage adds a pair in both orders of a commutative op).
+__device__ __forceinline__ float group16_sum(float x)
+{
+    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);   // row_half_mirror: lanes i <-> 7-i within 8
+    x += dpp<0x140>(x);   // row_mirror: lanes i <-> 15-i within 16
+    return x;
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64) by xor shuffles.
+template <int W>
+__device__ __forceinline__ float group_sum(float x)
+{
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1)
+        x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// ------------------------------------------------- one state row of a step
+//
+// A row of S (V x K, K contiguous) is spread over 16 lanes; lane c holds
+// columns 64*m + 4*c + e (m < K/64, e < 4), EPL = K/16 values.
+
+template <int EPL>
+__device__ __forceinline__ float rnorm16(const float (&x)[EPL], float eps)
+{
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = group16_sum(ss);
+    return 1.0f / sqrtf(ss + eps);
+}
+
+// S_row <- e^g S_row; u = S_row . k_hat; S_row += beta (v - u) k_hat
+template <int EPL>
+__device__ __forceinline__ void step_row(float (&s)[EPL], const float (&kh)[EPL], float v,
+                                         float decay, float beta)
+{
+    float u = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        s[e] = s[e] * decay;
+        u = __builtin_fmaf(s[e], kh[e], u);
+    }
+    u = group16_sum(u);
+    const float d = beta * (v - u);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        s[e] = __builtin_fmaf(d, kh[e], s[e]);
+}
+
+__device__ __forceinline__ int clamp_wp(int wp, int L, int T)
+{
+    return wp < 0 ? 0 : (wp > L - T ? L - T : wp);
+}
+
+__device__ __forceinline__ bool valid_slot(int s, int num_slots)
+{
+    return s >= 0 && s < num_slots;
+}
+
+}  // namespace gdn

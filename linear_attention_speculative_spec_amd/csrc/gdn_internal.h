@@ -1,0 +1,66 @@
+// gdn_internal.h -- host-side launch interface between the C ABI and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdnverify.h"
+
+namespace gdn {
+
+// Pointers of one call, untyped for activations (dtype from the shape).
+struct RingPtrs {
+    void* rawk;
+    void* rawv;
+    float* g;
+    float* beta;
+};
+
+struct CursorPtrs {
+    const int32_t* write_pos;
+    const int32_t* cache_base;
+    const int32_t* is_flush;
+};
+
+struct WindowPtrs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+};
+
+// Number of waves per verify workgroup (16 value columns each) and the
+// dynamic LDS it needs; 0 bytes if the shape cannot be served.
+int verify_waves(const gdn_shape& sh);
+size_t verify_lds_bytes(const gdn_shape& sh);
+size_t max_lds_bytes();
+
+hipError_t launch_verify(const gdn_shape& sh, const WindowPtrs& w, const float* S,
+                         const int32_t* slot_idx, const CursorPtrs& c, const RingPtrs& r,
+                         int write_ring, void* o, hipStream_t stream);
+
+hipError_t launch_fold(const gdn_shape& sh, int num_layers, float* S, const RingPtrs& r,
+                       const int32_t* slot_idx, const CursorPtrs& c, int only_flagged,
+                       hipStream_t stream);
+
+hipError_t launch_snapshot(const gdn_shape& sh, const WindowPtrs& w, const float* S,
+                           const int32_t* slot_idx, float* snap, void* o, const RingPtrs& r,
+                           const int32_t* write_pos, const int32_t* cache_base, int write_ring,
+                           hipStream_t stream);
+
+hipError_t launch_snapshot_commit(const gdn_shape& sh, const float* snap,
+                                  const int32_t* slot_idx, const int32_t* accept, float* S,
+                                  hipStream_t stream);
+
+hipError_t launch_advance(const gdn_shape& sh, const int32_t* slot_idx, const int32_t* accept,
+                          int32_t* write_pos, int32_t* cache_base, int32_t* is_flush,
+                          hipStream_t stream);
+
+hipError_t launch_reset(const gdn_shape& sh, const int32_t* slots, int32_t n, int32_t init_flush,
+                        int32_t* write_pos, int32_t* cache_base, int32_t* is_flush,
+                        hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects malformed arguments on the host before any launch.
+No call here reaches the GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_speculative_spec_amd import gdnverify as gv
+from linear_attention_speculative_spec_amd import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gdnverify.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_functions() == sorted(gv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gv._LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in (gv.GDN_OK, gv.GDN_EINVAL, gv.GDN_EUNSUPPORTED, gv.GDN_ELAUNCH):
+        assert gv.status_str(st) and gv.status_str(st) != "unknown status"
+    assert gv.status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIGS))
+def test_workload_shapes_are_valid(name):
+    assert gv.gdn_validate_shape(gv.GdnShape.from_layer(synth.CONFIGS[name])) == gv.GDN_OK
+
+
+BAD = [
+    (dict(L=48), gv.GDN_EINVAL),                      # ring length not a power of two
+    (dict(L=4, max_spec_len=4, T=4), gv.GDN_EINVAL),  # L < 2 * max_spec_len
+    (dict(T=5), gv.GDN_EINVAL),                       # T > max_spec_len
+    (dict(T=0), gv.GDN_EINVAL),
+    (dict(HV=24), gv.GDN_EINVAL),                     # HV % H != 0
+    (dict(act=7), gv.GDN_EINVAL),
+    (dict(B=-1), gv.GDN_EINVAL),
+    (dict(num_slots=0), gv.GDN_EINVAL),
+    (dict(l2norm_eps=-1.0), gv.GDN_EINVAL),
+    (dict(scale=float("inf")), gv.GDN_EINVAL),
+    (dict(K=96), gv.GDN_EUNSUPPORTED),
+    (dict(V=120), gv.GDN_EUNSUPPORTED),
+    (dict(V=272), gv.GDN_EUNSUPPORTED),
+    (dict(L=256), gv.GDN_EUNSUPPORTED),
+    (dict(max_spec_len=32, T=4, L=128), gv.GDN_EUNSUPPORTED),
+    (dict(K=256, L=128, max_spec_len=8, T=8), gv.GDN_EUNSUPPORTED),   # LDS over 160 KiB
+]
+
+
+@pytest.mark.parametrize("override,status", BAD)
+def test_invalid_shapes_are_rejected(override, status):
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"], **override)
+    assert gv.gdn_validate_shape(sh) == status
+    assert gv.gdn_ring_bytes(sh) == 0 and gv.gdn_snapshot_bytes(sh) == 0
+    # every entry point refuses it before touching the device
+    L = gv.lib()
+    n = None
+    assert L.gdn_spec_verify_ring(ctypes.byref(sh), *([n] * 16), 1, 1, n, n) == status
+    assert L.gdn_exact_fold(ctypes.byref(sh), 1, *([n] * 9), 1, n) == status
+    assert L.gdn_advance_cursors(ctypes.byref(sh), *([n] * 6)) == status
+    assert L.gdn_reset_cursors(ctypes.byref(sh), n, 0, 0, n, n, n, n) == status
+    assert L.gdn_recurrent_verify_snapshot(ctypes.byref(sh), *([n] * 17), 0, n) == status
+    assert L.gdn_snapshot_commit(ctypes.byref(sh), *([n] * 5)) == status
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    # every call below must be refused on the host: none may reach a launch
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"])
+    L = gv.lib()
+    n = None
+    good = ctypes.c_void_p(1 << 20)           # never dereferenced: rejected first
+    bad = ctypes.c_void_p((1 << 20) + 2)
+    args = [good] * 16
+    assert L.gdn_spec_verify_ring(ctypes.byref(sh), *([n] * 16), 1, 1, good, n) == gv.GDN_EINVAL
+    args[0] = bad                              # q misaligned
+    assert L.gdn_spec_verify_ring(ctypes.byref(sh), *args, 1, 1, good, n) == gv.GDN_EINVAL
+    # output aliasing an input
+    args = [good] * 16
+    assert L.gdn_spec_verify_ring(ctypes.byref(sh), *args, 1, 1, good, n) == gv.GDN_EINVAL
+    assert L.gdn_exact_fold(ctypes.byref(sh), 0, *([good] * 9), 1, n) == gv.GDN_EINVAL
+    assert L.gdn_reset_cursors(ctypes.byref(sh), good, -1, 0, good, good, good, n) == gv.GDN_EINVAL
+    assert L.gdn_advance_cursors(ctypes.byref(sh), good, n, good, good, good, n) == gv.GDN_EINVAL
+    assert L.gdn_snapshot_commit(ctypes.byref(sh), good, good, n, good, n) == gv.GDN_EINVAL
+
+
+def test_footprints():
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b256"])
+    rec = 16 * 128 * 2 + 32 * (128 * 2 + 8)          # 12544 bytes per slot-record
+    assert rec == 12544
+    assert gv.gdn_ring_bytes(sh) == 512 * 64 * rec
+    assert gv.gdn_snapshot_bytes(sh) == 256 * 4 * 32 * 128 * 128 * 4
+    assert gv.gdn_snapshot_bytes(sh) > 5 * gv.gdn_ring_bytes(sh)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(gv, "_lib", None)
+    monkeypatch.setattr(gv, "_LIB_PATH", "/nonexistent/libgdnverify.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        gv.lib()
