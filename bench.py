@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN ring spec-verify step on one MI355X.
+
+Workload: one Qwen3-Next-shaped GDN layer, B=256 rows over 512 state slots
+(fp32 checkpoint S[512,32,128,128] = 1.07 GB), H=16 qk-heads, HV=32 value
+heads, K=V=128, T=4 drafts, ring L=64, bf16 activations; seeded synthetic
+inputs with random ring cursors (history pre-filled through the library's own
+verify).  A step is the whole hot path for one batch: exact fold of the rows
+flagged for flush, the ring verify (outputs of all T drafts + ring write),
+and the cursor advance by synthetic accept counts U{0..T}.
+
+Prints one JSON line: draft tokens/s per layer, the verify kernel's achieved
+HBM GB/s against the 8 TB/s peak (algorithmic bytes / event-timed duration),
+the snapshot baseline for comparison and the fp64 CPU oracle's rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "qwen3next_b256"
+HBM_PEAK_GBS = 8000.0
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "verify_kernel_qwen3next_b256.md")
+VERIFY_SRC = os.path.join(ROOT, "linear_attention_speculative_spec_amd", "csrc", "gdn_verify.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-snapshot", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def record_bytes(sh) -> int:
+    eb = 2 if sh.act == "bf16" else 4
+    return sh.H * sh.K * eb + sh.HV * (sh.V * eb + 8)
+
+
+def verify_alg_bytes(sh, hist: np.ndarray) -> int:
+    """Bytes the verify must move for one call (each counted once).
+
+    S0 rows read + committed history read + window in + outputs + ring write
+    of the window + slot indices and cursors."""
+    eb = 2 if sh.act == "bf16" else 4
+    B, T = sh.B, sh.T
+    s0 = B * sh.HV * sh.V * sh.K * 4
+    win = B * T * (2 * sh.H * sh.K + sh.HV * sh.V + 2 * sh.HV) * eb
+    out = B * T * sh.HV * sh.V * eb
+    ring_w = B * T * record_bytes(sh)
+    hist_r = int(hist.sum()) * record_bytes(sh)
+    return s0 + hist_r + win + out + ring_w + B * 16
+
+
+def fold_alg_bytes(sh, folded_records: np.ndarray) -> int:
+    n = len(folded_records)
+    return n * 2 * sh.HV * sh.V * sh.K * 4 + int(folded_records.sum()) * record_bytes(sh)
+
+
+def snapshot_alg_bytes(sh) -> int:
+    eb = 2 if sh.act == "bf16" else 4
+    B, T = sh.B, sh.T
+    return (B * sh.HV * sh.V * sh.K * 4 + B * T * sh.HV * sh.V * sh.K * 4 +
+            B * T * (2 * sh.H * sh.K + sh.HV * sh.V + 2 * sh.HV) * eb + B * T * sh.HV * sh.V * eb)
+
+
+def traffic_from_profile():
+    """HBM bytes per verify launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        text = open(PROFILE_SUMMARY).read()
+    except OSError:
+        return None
+    src_hash = hashlib.sha256(open(VERIFY_SRC, "rb").read()).hexdigest()[:16]
+    m_hash = re.search(r"source sha256\[:16\]: `([0-9a-f]{16})`", text)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\): ([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = int(os.environ.get("OMP_NUM_THREADS", n) or n)
+    return max(1, min(n, cap))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the path shards by rows and value heads with no exchange; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_speculative_spec_amd import gdnverify as gv
+    from linear_attention_speculative_spec_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    sh = synth.CONFIGS[WORKLOAD]
+    gs = gv.GdnShape.from_layer(sh)
+    gv.lib()   # fail loudly if the HIP library is missing
+    rng = synth.make_rng(args.seed)
+
+    t0 = time.time()
+    log(f"[bench] generating {WORKLOAD} inputs")
+    params = synth.layer_params(rng, sh)
+    slots = synth.slot_choice(rng, sh)
+    cd = synth.random_cursors(rng, sh)
+    n_hist = int(cd.write_pos[slots].max())
+    hist_windows = synth.history_windows(rng, sh, n_hist)
+    n_pool = 4
+    pool = [synth.window(rng, sh) for _ in range(n_pool)]
+    n_steps = args.warmup + args.steps
+    accepts = synth.accept_counts(rng, sh.B, sh.T, n_steps)
+
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)  # noqa: E731
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)    # noqa: E731
+
+    S = f32(params.S0)
+    A_log, dt_bias = f32(params.A_log), f32(params.dt_bias)
+    rawk = torch.zeros(sh.num_slots, sh.H, sh.L, sh.K, dtype=torch.bfloat16, device=dev)
+    rawv = torch.zeros(sh.num_slots, sh.HV, sh.L, sh.V, dtype=torch.bfloat16, device=dev)
+    rg = torch.zeros(sh.num_slots, sh.HV, sh.L, dtype=torch.float32, device=dev)
+    rb = torch.zeros_like(rg)
+    dslots = i32(slots)
+    wins = [[bf(x) for x in (w.q, w.k, w.v, w.a, w.b)] for w in pool]
+
+    # pre-fill the rings: one recorded token per call through the verify itself
+    log(f"[bench] pre-filling rings with up to {n_hist} records ({time.time() - t0:.1f}s)")
+    gs1 = gs.replace(T=1)
+    scratch = torch.empty(sh.B, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    zeros = i32(np.zeros(sh.num_slots))
+    base_d = i32(cd.cache_base)
+    for r, w in enumerate(hist_windows):
+        sl = np.where(cd.write_pos[slots] > r, slots, -1).astype(np.int32)
+        wp_r = i32(np.full(sh.num_slots, r))
+        gv.gdn_spec_verify_ring(gs1, *[bf(x) for x in (w.q, w.k, w.v, w.a, w.b)], A_log,
+                                dt_bias, S, i32(sl), wp_r, base_d, zeros, rawk, rawv, rg, rb,
+                                1, 0, scratch)
+    del hist_windows
+    wp0 = cd.write_pos.astype(np.int32)
+    fl0 = (wp0 + 2 * sh.max_spec > sh.L).astype(np.int32)
+    cur = [i32(wp0), i32(cd.cache_base), i32(fl0)]
+    acc_d = [i32(a) for a in accepts]
+    o = torch.empty(sh.B * sh.T, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        w = wins[i % n_pool]
+        if ev is not None:
+            ev[0].record()
+        gv.gdn_exact_fold(gs, 1, S, rawk, rawv, rg, rb, dslots, cur[0], cur[1], cur[2], 1)
+        if ev is not None:
+            ev[1].record()
+        gv.gdn_spec_verify_ring(gs, *w, A_log, dt_bias, S, dslots, cur[0], cur[1], cur[2],
+                                rawk, rawv, rg, rb, 1, 0, o)
+        if ev is not None:
+            ev[2].record()
+        gv.gdn_advance_cursors(gs, dslots, acc_d[i], cur[0], cur[1], cur[2])
+
+    # dry run of the same trajectory to learn each step's history lengths
+    saved = [S.clone(), rawk.clone(), rawv.clone(), rg.clone(), rb.clone(),
+             [c.clone() for c in cur]]
+    hist_per_step, fold_per_step = [], []
+    for i in range(n_steps):
+        wp = cur[0].cpu().numpy()[slots]
+        fl = cur[2].cpu().numpy()[slots]
+        hist_per_step.append(np.where(fl != 0, 0, np.clip(wp, 0, sh.L - sh.T)))
+        fold_per_step.append(np.clip(wp[fl != 0], 0, sh.L - sh.T))
+        step(i)
+    torch.cuda.synchronize()
+
+    def restore():
+        S.copy_(saved[0]), rawk.copy_(saved[1]), rawv.copy_(saved[2])
+        rg.copy_(saved[3]), rb.copy_(saved[4])
+        for c, s0 in zip(cur, saved[5]):
+            c.copy_(s0)
+        torch.cuda.synchronize()
+
+    restore()
+    log(f"[bench] warmup {args.warmup} steps ({time.time() - t0:.1f}s)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    verify_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    fold_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    timed = range(args.warmup, n_steps)
+    vbytes = np.array([verify_alg_bytes(sh, hist_per_step[i]) for i in timed], dtype=np.float64)
+    fbytes = np.array([fold_alg_bytes(sh, fold_per_step[i]) for i in timed], dtype=np.float64)
+    v_avg_us = float(verify_ms.mean() * 1e3)
+    achieved = float(vbytes.mean() / (verify_ms.mean() * 1e-3) / 1e9)
+    tokens = sh.B * sh.T
+    log(f"[bench] step {ms_step * 1e3:.1f} us, verify {v_avg_us:.1f} us "
+        f"({achieved:.0f} GB/s), fold {fold_ms.mean() * 1e3:.1f} us")
+
+    result = {
+        "metric": "GDN verify draft tokens/s per layer",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random cursors, ring pre-filled by the library's verify)",
+        "config": {"workload": "GDN layer B=256 rows, 512 slots, H=16, HV=32, K=V=128, "
+                               "T=4, L=64, bf16 act, fp32 state",
+                   "global_batch": sh.B, "draft_tokens": sh.T, "ring_len": sh.L,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "verify_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_from_profile(),
+            "alg_bytes_per_launch": float(vbytes.mean()),
+            "avg_launch_us": v_avg_us,
+        },
+        "fold": {"avg_launch_us": float(fold_ms.mean() * 1e3),
+                 "alg_bytes_per_launch": float(fbytes.mean()),
+                 "flagged_rows_per_step": float(np.mean([len(fold_per_step[i]) for i in timed]))},
+        "memory": {"ring_bytes_per_layer": gv.gdn_ring_bytes(gs),
+                   "snapshot_bytes_per_layer": gv.gdn_snapshot_bytes(gs),
+                   "checkpoint_bytes_per_layer": sh.num_slots * sh.HV * sh.V * sh.K * 4},
+    }
+
+    if not args.no_snapshot:
+        snap = torch.empty(sh.B, sh.T, sh.HV, sh.V, sh.K, dtype=torch.float32, device=dev)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for i in range(3):
+            gv.gdn_recurrent_verify_snapshot(gs, *wins[i % n_pool], A_log, dt_bias, S, dslots,
+                                             snap, o)
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record()
+        for i in range(reps):
+            gv.gdn_recurrent_verify_snapshot(gs, *wins[i % n_pool], A_log, dt_bias, S, dslots,
+                                             snap, o)
+        e1.record()
+        for i in range(reps):
+            gv.gdn_snapshot_commit(gs, snap, dslots, acc_d[i % n_steps], saved[0])
+        e2.record()
+        torch.cuda.synchronize()
+        snap_us = e0.elapsed_time(e1) / reps * 1e3
+        commit_us = e1.elapsed_time(e2) / reps * 1e3
+        sb = snapshot_alg_bytes(sh)
+        result["snapshot_baseline"] = {
+            "verify_us": snap_us, "commit_us": commit_us,
+            "alg_bytes_per_launch": sb, "achieved_GBs": sb / (snap_us * 1e-6) / 1e9,
+            "draft_tokens_per_s": tokens / ((snap_us + commit_us) * 1e-6)}
+        del snap
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sh, args.seed, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(sh, seed, budget_s):
+    """The fp64 oracle on the same workload: the same seeded layer, cursors
+    and pre-filled history, verifying whole batches of rows on the host."""
+    import oracle
+    from oracle.cursors import CursorState
+    from linear_attention_speculative_spec_amd import synth
+
+    rng = synth.make_rng(seed)
+    params = synth.layer_params(rng, sh)
+    slots = synth.slot_choice(rng, sh)
+    cd = synth.random_cursors(rng, sh)
+    n_hist = int(cd.write_pos[slots].max())
+    hist_windows = synth.history_windows(rng, sh, n_hist)
+    win = synth.window(rng, sh)
+    rows = np.arange(sh.B)
+    osh = sh.replace(num_slots=sh.B)
+    orc = oracle.OracleLayer(osh, params.A_log, params.dt_bias, params.S0[slots])
+    del params
+    oslots = np.arange(sh.B, dtype=np.int32)
+    cur = CursorState(np.zeros(sh.B, np.int32), cd.cache_base[slots].copy(),
+                      np.zeros(sh.B, np.int32))
+    to64 = lambda w: tuple(synth.act_to_f64(x, sh.act) for x in (w.q, w.k, w.v, w.a, w.b))  # noqa: E731
+    for r, w in enumerate(hist_windows):
+        cur.write_pos[:] = r
+        sl = np.where(cd.write_pos[slots] > r, oslots, -1).astype(np.int32)
+        orc.write_ring(cur, sl, to64(w), T=1)
+    del hist_windows
+    wp = cd.write_pos[slots].astype(np.int32)
+    cur = CursorState(wp, cd.cache_base[slots].copy(),
+                      (wp + 2 * sh.max_spec > sh.L).astype(np.int32))
+    w64 = to64(win)
+    nt = cpu_threads()
+    # only unflagged rows so the oracle's checkpoint stays as generated
+    cur.is_flush[:] = 0
+    reps, t_used = 0, 0.0
+    while t_used < budget_s:
+        t1 = time.perf_counter()
+        orc.verify(cur, oslots, w64, write_ring=False, fold_flagged=False, nthreads=nt)
+        t_used += time.perf_counter() - t1
+        reps += 1
+    return {"value": reps * sh.B * sh.T / t_used, "unit": "draft tokens/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"{reps} full verifies of the B={sh.B} batch (all {sh.HV} value heads, "
+                      f"history replay + {sh.T} drafts, fp64), {t_used:.1f} s wall on {nt} threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -70,8 +70,9 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * pages' configuration checks: PR #28695 summary, server_args snippet: ring
  * length at least twice the draft count; PR #36821 summary, ring view checks):
  *   B >= 0; 1 <= T <= max_spec_len <= 16; L a power of two, 2*max_spec_len <= L
- *   <= 128; H >= 1; HV % H == 0; K in {64, 128, 256}; V % 16 == 0, 16 <= V <= 256;
- *   num_slots >= 1; act in {GDN_F32, GDN_BF16}; l2norm_eps >= 0, finite scale.
+ *   <= 128; H >= 1; HV % H == 0; K in {64, 128, 256} (K = 256 only with L <= 64);
+ *   V % 16 == 0, 16 <= V <= 256; 0 <= B <= 65535; num_slots >= 1;
+ *   act in {GDN_F32, GDN_BF16}; l2norm_eps >= 0; finite scale and threshold.
  * Anything else returns GDN_EINVAL (malformed) or GDN_EUNSUPPORTED.
  */
 typedef struct gdn_shape {
@@ -109,9 +110,8 @@ typedef struct gdn_shape {
  *   and beta used by the kernel.  Nothing else in the ring is written and the
  *   outputs are bitwise identical with write_ring = 0.
  * S is never written for unflagged rows; cursors are never written.
- * o must not alias any input.  With write_ring = 0 the ring pointers may be
- * NULL only if no row is flagged or fold_flagged = 0 and hist reads nothing
- * (they are always read for history); pass them whenever any history exists.
+ * o must not alias any input.  The ring pointers are always required (the
+ * history is read from them even when write_ring = 0).
  */
 int gdn_spec_verify_ring(const gdn_shape *shape,
                          const void *q, const void *k, const void *v,

@@ -46,6 +46,8 @@ int check_shape(const gdn_shape* sh)
         return GDN_EUNSUPPORTED;
     if (s.max_spec_len > 16 || s.L > 128)
         return GDN_EUNSUPPORTED;
+    if (s.K == 256 && s.L > 64)          // verify staging would exceed the register budget
+        return GDN_EUNSUPPORTED;
     if (s.B > 65535 || s.HV > 65535)
         return GDN_EUNSUPPORTED;
     if (verify_lds_bytes(s) > max_lds_bytes())

@@ -32,9 +32,8 @@ struct WindowPtrs {
     const float* dt_bias;
 };
 
-// Number of waves per verify workgroup (16 value columns each) and the
-// dynamic LDS it needs; 0 bytes if the shape cannot be served.
-int verify_waves(const gdn_shape& sh);
+// Value columns per verify workgroup and the dynamic LDS it needs.
+int verify_tile_cols(const gdn_shape& sh);
 size_t verify_lds_bytes(const gdn_shape& sh);
 size_t max_lds_bytes();
 

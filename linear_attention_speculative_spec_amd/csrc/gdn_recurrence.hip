@@ -59,29 +59,84 @@ __device__ __forceinline__ void load_cols(const typename Act::storage* row, int 
     }
 }
 
-// grid (V/16, B, HV * num_layers), block 256
+// Per-record quantities that do not depend on the state: the normalised key
+// (columns of this lane) and the decay e^g.  Computed by one 16-lane group
+// per record, with the same lane layout and reduction tree everywhere, so the
+// fold and the snapshot verify see identical bits.
+template <int EPL>
+__device__ __forceinline__ void prep_key(const float (&kc)[EPL], float eps, float (&kh)[EPL])
+{
+    const float rn = rnorm16<EPL>(kc, eps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        kh[e] = kc[e] * rn;
+}
+
+template <int K>
+__device__ __forceinline__ void load_cols_f32(const float* row, int c, float (&x)[K / 16])
+{
+#pragma unroll
+    for (int m = 0; m < K / 64; ++m) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(row + 64 * m + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            x[4 * m + e] = t[e];
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void store_cols_f32(float* row, int c, const float (&x)[K / 16])
+{
+#pragma unroll
+    for (int m = 0; m < K / 64; ++m)
+        *reinterpret_cast<f32x4*>(row + 64 * m + 4 * c) =
+            f32x4{x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
+}
+
+// Records of the fold are staged through LDS in batches of kFoldBatch,
+// double-buffered: the loads of batch i+1 are in flight while the sequential
+// steps of batch i run from LDS.
+constexpr int kFoldBatch = 16;
+
 template <class Act, int K>
-__global__ __launch_bounds__(256) void fold_kernel(const RecParams p)
+struct FoldStage {
+    static constexpr int KU = K * Act::bytes / 16;            // 16-byte units per key
+    static constexpr int VU = 16 * Act::bytes / 16;           // units of 16 values
+    static constexpr int KUB = kFoldBatch * KU;               // key units per batch
+    static constexpr int VUB = kFoldBatch * VU;
+    static constexpr int KPT = (KUB + 255) / 256;             // key units per thread
+};
+
+template <class Act, int K>
+struct FoldShared {
+    uint4 kbuf[2][FoldStage<Act, K>::KUB];          // raw keys of a batch
+    uint4 vbuf[2][FoldStage<Act, K>::VUB];          // this tile's 16 values per record
+    float gbuf[2][kFoldBatch], bbuf[2][kFoldBatch];  // gate (then decay) and beta
+    float khs[2][kFoldBatch][K];                     // normalised keys
+};
+
+// Fold of one work item: the n committed records of slot s into 16 rows
+// (tile) of one layer's value head hv.  Called uniformly by the workgroup.
+template <class Act, int K>
+__device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int n, int base,
+                          int layer, int hv, int tile)
 {
     using st = typename Act::storage;
+    using FS = FoldStage<Act, K>;
     constexpr int EPL = K / 16;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int RB = kFoldBatch;
+    auto& kbuf = sh.kbuf;
+    auto& vbuf = sh.vbuf;
+    auto& gbuf = sh.gbuf;
+    auto& bbuf = sh.bbuf;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, grp = lane >> 4;
-    const int vrow = blockIdx.x * 16 + w * 4 + grp;
-    const int b = blockIdx.y;
-    const int layer = blockIdx.z / p.HV, hv = blockIdx.z - layer * p.HV;
+    const int row16 = w * 4 + grp;                 // row within the 16-row tile
+    const int vrow = tile * 16 + row16;
     const int h = hv / (p.HV / p.H);
     const int L = p.L;
-
-    const int s = p.slot_idx[b];
-    if (!valid_slot(s, p.num_slots))
-        return;
-    if (p.only_flagged && p.is_flush[s] == 0)
-        return;
-    const int n = clamp_wp(p.write_pos[s], L, p.T);
-    if (n == 0)
-        return;
-    const int base = p.cache_base[s];
 
     const size_t ring_slots = static_cast<size_t>(p.num_slots) * L;
     float* Srow = p.S + static_cast<size_t>(layer) * p.num_slots * p.HV * p.V * K +
@@ -89,56 +144,148 @@ __global__ __launch_bounds__(256) void fold_kernel(const RecParams p)
     const st* rk = static_cast<const st*>(p.rawk) + static_cast<size_t>(layer) * ring_slots * p.H * K +
                    (static_cast<size_t>(s) * p.H + h) * L * K;
     const st* rv = static_cast<const st*>(p.rawv) + static_cast<size_t>(layer) * ring_slots * p.HV * p.V +
-                   (static_cast<size_t>(s) * p.HV + hv) * L * p.V + vrow;
+                   (static_cast<size_t>(s) * p.HV + hv) * L * p.V + tile * 16;
     const size_t gofs = static_cast<size_t>(layer) * ring_slots * p.HV +
                         (static_cast<size_t>(s) * p.HV + hv) * L;
     const float* rg = p.rg + gofs;
     const float* rb = p.rb + gofs;
 
-    float sv[EPL];
+    // registers of one batch in flight
+    uint4 kreg[FS::KPT];
+    uint4 vreg;
+    float greg;
+    auto issue = [&](int bi) {
 #pragma unroll
-    for (int m = 0; m < K / 64; ++m) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(Srow + 64 * m + 4 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sv[4 * m + e] = t[e];
-    }
-
-    // records are independent of the state: fetch one ahead
-    float kn[EPL], vn, gn, bn;
-    {
-        const int ph = base & (L - 1);
-        load_cols<Act, K>(rk + static_cast<size_t>(ph) * K, c, kn);
-        vn = Act::load(rv + static_cast<size_t>(ph) * p.V);
-        gn = rg[ph];
-        bn = rb[ph];
-    }
-    for (int j = 0; j < n; ++j) {
-        float kc[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            kc[e] = kn[e];
-        const float vc = vn, gc = gn, bc = bn;
-        if (j + 1 < n) {
-            const int ph = (base + j + 1) & (L - 1);
-            load_cols<Act, K>(rk + static_cast<size_t>(ph) * K, c, kn);
-            vn = Act::load(rv + static_cast<size_t>(ph) * p.V);
-            gn = rg[ph];
-            bn = rb[ph];
+        for (int i = 0; i < FS::KPT; ++i) {
+            const int u = i * 256 + tid;
+            const int j = bi * RB + u / FS::KU;
+            kreg[i] = uint4{0u, 0u, 0u, 0u};
+            if (u < FS::KUB && j < n) {
+                const int ph = (base + j) & (L - 1);
+                kreg[i] = reinterpret_cast<const uint4*>(rk + static_cast<size_t>(ph) * K)[u % FS::KU];
+            }
         }
-        const float rn = rnorm16<EPL>(kc, p.eps);
-        float kh[EPL];
+        vreg = uint4{0u, 0u, 0u, 0u};
+        greg = 0.0f;
+        if (tid < FS::VUB) {
+            const int j = bi * RB + tid / FS::VU;
+            if (j < n) {
+                const int ph = (base + j) & (L - 1);
+                vreg = reinterpret_cast<const uint4*>(rv + static_cast<size_t>(ph) * p.V)[tid % FS::VU];
+            }
+        } else if (tid >= 128 && tid < 128 + 2 * RB) {
+            const int r = tid - 128;
+            const int j = bi * RB + (r % RB);
+            if (j < n) {
+                const int ph = (base + j) & (L - 1);
+                greg = r < RB ? rg[ph] : rb[ph];
+            }
+        }
+    };
+    auto commit = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            kh[e] = kc[e] * rn;
-        step_row<EPL>(sv, kh, vc, expf(gc), bc);
+        for (int i = 0; i < FS::KPT; ++i) {
+            const int u = i * 256 + tid;
+            if (u < FS::KUB)
+                kbuf[buf][u] = kreg[i];
+        }
+        if (tid < FS::VUB) {
+            vbuf[buf][tid] = vreg;
+        } else if (tid >= 128 && tid < 128 + 2 * RB) {
+            const int r = tid - 128;
+            if (r < RB)
+                gbuf[buf][r] = greg;
+            else
+                bbuf[buf][r - RB] = greg;
+        }
+    };
+
+    // 16 lane groups normalise the 16 keys of a batch in parallel
+    auto prep = [&](int buf, int cnt) {
+        const int jj = row16;
+        if (jj < cnt) {
+            float kc[EPL], kh[EPL];
+            const st* kb = reinterpret_cast<const st*>(kbuf[buf]);
+            load_cols<Act, K>(kb + jj * K, c, kc);
+            prep_key<EPL>(kc, p.eps, kh);
+            store_cols_f32<K>(sh.khs[buf][jj], c, kh);
+            if (c == 0)
+                gbuf[buf][jj] = expf(gbuf[buf][jj]);
+        }
+    };
+
+    issue(0);
+    float sv[EPL];
+    load_cols_f32<K>(Srow, c, sv);
+    commit(0);
+    __syncthreads();
+    prep(0, min(RB, n));
+    __syncthreads();
+
+    const int nbatch = (n + RB - 1) / RB;
+    for (int bi = 0; bi < nbatch; ++bi) {
+        const int buf = bi & 1;
+        if (bi + 1 < nbatch)
+            issue(bi + 1);
+        const int cnt = min(RB, n - bi * RB);
+        const st* vb = reinterpret_cast<const st*>(vbuf[buf]);
+        for (int jj = 0; jj < cnt; ++jj) {
+            float kh[EPL];
+            load_cols_f32<K>(sh.khs[buf][jj], c, kh);
+            step_row<EPL>(sv, kh, Act::load(vb + jj * 16 + row16), gbuf[buf][jj], bbuf[buf][jj]);
+        }
+        if (bi + 1 < nbatch) {
+            commit(buf ^ 1);
+            __syncthreads();
+            prep(buf ^ 1, min(RB, n - (bi + 1) * RB));
+        }
+        __syncthreads();
     }
 
-#pragma unroll
-    for (int m = 0; m < K / 64; ++m)
-        *reinterpret_cast<f32x4*>(Srow + 64 * m + 4 * c) =
-            f32x4{sv[4 * m], sv[4 * m + 1], sv[4 * m + 2], sv[4 * m + 3]};
+    store_cols_f32<K>(Srow, c, sv);
 }
+
+// Persistent fold: every workgroup compacts the rows to fold (in chunks of
+// kFoldRows) into LDS, then strides over the work items (row, layer, value
+// head, 16-row tile).  Rows with nothing to fold cost no workgroup.
+constexpr int kFoldRows = 1024;
+
+template <class Act, int K>
+__global__ __launch_bounds__(256) void fold_kernel(const RecParams p, int num_layers)
+{
+    __shared__ FoldShared<Act, K> sh;
+    __shared__ int rows[kFoldRows];
+    __shared__ int nrows;
+    const int tid = threadIdx.x;
+    const int tiles = p.V / 16;
+    const int per_row = num_layers * p.HV * tiles;
+    for (int c0 = 0; c0 < p.B; c0 += kFoldRows) {
+        if (tid == 0)
+            nrows = 0;
+        __syncthreads();
+        for (int r = c0 + tid; r < min(c0 + kFoldRows, p.B); r += 256) {
+            const int s = p.slot_idx[r];
+            if (valid_slot(s, p.num_slots) && (!p.only_flagged || p.is_flush[s] != 0) &&
+                clamp_wp(p.write_pos[s], p.L, p.T) > 0)
+                rows[atomicAdd(&nrows, 1)] = r;
+        }
+        __syncthreads();
+        const int nitems = nrows * per_row;
+        for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+            const int row = rows[it / per_row];
+            const int rem = it % per_row;
+            const int tile = rem % tiles;
+            const int lh = rem / tiles;              // layer * HV + hv
+            const int s = p.slot_idx[row];
+            fold_item<Act, K>(p, sh, s, clamp_wp(p.write_pos[s], p.L, p.T), p.cache_base[s],
+                              lh / p.HV, lh % p.HV, tile);
+        }
+        __syncthreads();
+    }
+}
+
+// Window of the snapshot verify, staged once through LDS (T <= 16 tokens).
+constexpr int kMaxT = 16;
 
 // grid (V/16, B, HV), block 256
 template <class Act, int K>
@@ -146,9 +293,18 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
 {
     using st = typename Act::storage;
     constexpr int EPL = K / 16;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int KU = K * Act::bytes / 16;      // 16-byte units per key/query row
+    constexpr int VU = 16 * Act::bytes / 16;     // units of the tile's 16 values
+    __shared__ uint4 kq[2 * kMaxT * KU];         // raw keys then queries
+    __shared__ uint4 vv[kMaxT * VU];
+    __shared__ float gs[kMaxT], bs[kMaxT];       // decay e^g and beta
+    __shared__ float khs[kMaxT][K], qhs[kMaxT][K];   // normalised keys / queries
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, grp = lane >> 4;
-    const int vrow = blockIdx.x * 16 + w * 4 + grp;
+    const int row16 = w * 4 + grp;
+    const int vrow = blockIdx.x * 16 + row16;
     const int b = blockIdx.y, hv = blockIdx.z;
     const int G = p.HV / p.H, h = hv / G;
     const int T = p.T, L = p.L;
@@ -171,28 +327,60 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
         wpc = clamp_wp(p.write_pos[s], L, T);
         base = p.cache_base[s];
     }
-    const float A_log = p.A_log[hv], dt_bias = p.dt_bias[hv];
+    const size_t tok0 = static_cast<size_t>(b) * T;
 
-    for (int t = 0; t < T; ++t) {
-        const size_t tok = static_cast<size_t>(b) * T + t;
-        const st* krow = static_cast<const st*>(p.k) + (tok * p.H + h) * K;
-        const st* qrow = static_cast<const st*>(p.q) + (tok * p.H + h) * K;
-        const st* vptr = static_cast<const st*>(p.v) + (tok * p.HV + hv) * p.V + vrow;
-        float kc[EPL], qc[EPL];
-        load_cols<Act, K>(krow, c, kc);
-        load_cols<Act, K>(qrow, c, qc);
-        const float vc = Act::load(vptr);
+    // ---- stage the window: keys, queries, this tile's values, gates
+    for (int u = tid; u < 2 * T * KU; u += 256) {
+        const int r = u / KU, part = u % KU;          // r < T: key t=r; else query t=r-T
+        const st* src = (r < T ? static_cast<const st*>(p.k) : static_cast<const st*>(p.q)) +
+                        ((tok0 + (r < T ? r : r - T)) * p.H + h) * K;
+        kq[u] = reinterpret_cast<const uint4*>(src)[part];
+    }
+    for (int u = tid; u < T * VU; u += 256) {
+        const st* src = static_cast<const st*>(p.v) + ((tok0 + u / VU) * p.HV + hv) * p.V +
+                        blockIdx.x * 16;
+        vv[u] = reinterpret_cast<const uint4*>(src)[u % VU];
+    }
+    if (tid < T) {
+        const size_t tok = tok0 + tid;
         float g, beta;
         gdn_gate(Act::load(static_cast<const st*>(p.a) + tok * p.HV + hv),
-                 Act::load(static_cast<const st*>(p.b) + tok * p.HV + hv), A_log, dt_bias,
-                 p.softplus_threshold, g, beta);
+                 Act::load(static_cast<const st*>(p.b) + tok * p.HV + hv), p.A_log[hv],
+                 p.dt_bias[hv], p.softplus_threshold, g, beta);
+        gs[tid] = g;
+        bs[tid] = beta;
+        if (p.write_ring && blockIdx.x == 0) {
+            const size_t gi = (static_cast<size_t>(s) * p.HV + hv) * L + ((base + wpc + tid) & (L - 1));
+            p.wg[gi] = g;
+            p.wbeta[gi] = beta;
+        }
+    }
+    __syncthreads();
 
-        const float rn = rnorm16<EPL>(kc, p.eps);
-        float kh[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            kh[e] = kc[e] * rn;
-        step_row<EPL>(sv, kh, vc, expf(g), beta);
+    const st* kst = reinterpret_cast<const st*>(kq);
+    const st* vst = reinterpret_cast<const st*>(vv);
+    // 16 lane groups normalise the window's keys and queries in parallel
+    if (row16 < T) {
+        const int t = row16;
+        float xc[EPL], xh[EPL];
+        load_cols<Act, K>(kst + static_cast<size_t>(t) * K, c, xc);
+        prep_key<EPL>(xc, p.eps, xh);
+        store_cols_f32<K>(khs[t], c, xh);
+        load_cols<Act, K>(kst + static_cast<size_t>(T + t) * K, c, xc);
+        prep_key<EPL>(xc, p.eps, xh);
+        store_cols_f32<K>(qhs[t], c, xh);
+        if (c == 0)
+            gs[t] = expf(gs[t]);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = tok0 + t;
+        float kh[EPL], qh[EPL];
+        load_cols_f32<K>(khs[t], c, kh);
+        load_cols_f32<K>(qhs[t], c, qh);
+        const float vc = Act::load(vst + t * 16 + row16);
+        step_row<EPL>(sv, kh, vc, gs[t], bs[t]);
 
         float* srow = p.snap + (((static_cast<size_t>(b) * T + t) * p.HV + hv) * p.V + vrow) * K;
 #pragma unroll
@@ -200,11 +388,10 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
             *reinterpret_cast<f32x4*>(srow + 64 * m + 4 * c) =
                 f32x4{sv[4 * m], sv[4 * m + 1], sv[4 * m + 2], sv[4 * m + 3]};
 
-        const float rq = rnorm16<EPL>(qc, p.eps);
         float dot = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            dot = __builtin_fmaf(sv[e], qc[e] * rq, dot);
+            dot = __builtin_fmaf(sv[e], qh[e], dot);
         dot = group16_sum(dot);
         if (c == 0)
             static_cast<st*>(p.o)[(tok * p.HV + hv) * p.V + vrow] = Act::from_f32(p.scale * dot);
@@ -215,16 +402,11 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
                 st* dk = static_cast<st*>(p.wrawk) + ((static_cast<size_t>(s) * p.H + h) * L + ph) * K;
 #pragma unroll
                 for (int m = 0; m < K / 64; ++m)
-                    copy4<Act>(dk + 64 * m + 4 * c, krow + 64 * m + 4 * c);
+                    copy4<Act>(dk + 64 * m + 4 * c, kst + static_cast<size_t>(t) * K + 64 * m + 4 * c);
             }
             if (c == 0)
                 static_cast<st*>(p.wrawv)[((static_cast<size_t>(s) * p.HV + hv) * L + ph) * p.V + vrow] =
-                    *vptr;
-            if (blockIdx.x == 0 && threadIdx.x == 0) {
-                const size_t gi = (static_cast<size_t>(s) * p.HV + hv) * L + ph;
-                p.wg[gi] = g;
-                p.wbeta[gi] = beta;
-            }
+                    vst[t * 16 + row16];
         }
     }
 }
@@ -253,11 +435,13 @@ template <class Act>
 static hipError_t launch_fold_act(const gdn_shape& sh, int num_layers, const RecParams& p,
                                   hipStream_t stream)
 {
-    const dim3 grid(sh.V / 16, sh.B, sh.HV * num_layers);
+    // persistent grid: enough workgroups to fill the chip, never more than items
+    const long long items = static_cast<long long>(sh.B) * num_layers * sh.HV * (sh.V / 16);
+    const unsigned grid = static_cast<unsigned>(items < 2048 ? items : 2048);
     switch (sh.K) {
-    case 64: hipLaunchKernelGGL((fold_kernel<Act, 64>), grid, dim3(256), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((fold_kernel<Act, 128>), grid, dim3(256), 0, stream, p); break;
-    case 256: hipLaunchKernelGGL((fold_kernel<Act, 256>), grid, dim3(256), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((fold_kernel<Act, 64>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
+    case 128: hipLaunchKernelGGL((fold_kernel<Act, 128>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
+    case 256: hipLaunchKernelGGL((fold_kernel<Act, 256>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
