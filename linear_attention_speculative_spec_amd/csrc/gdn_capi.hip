@@ -50,6 +50,9 @@ int check_shape(const gdn_shape* sh)
         return GDN_EUNSUPPORTED;
     if (s.B > 65535 || s.HV > 65535)
         return GDN_EUNSUPPORTED;
+    // work items (row, value head, value tile) are counted in 32-bit ints
+    if (static_cast<long long>(s.B) * s.HV * (s.V / 16) > 0x7FFFFFFFLL)
+        return GDN_EUNSUPPORTED;
     if (verify_lds_bytes(s) > max_lds_bytes())
         return GDN_EUNSUPPORTED;
     return GDN_OK;

@@ -19,34 +19,33 @@
 // the n x V deltas are never formed.
 //
 // Execution: a persistent grid; each workgroup (8 waves) strides over items
-// (row, value head, value tile of BV columns) and pipelines them:
-//   * the raw keys/queries (X), the value tile and the gate inputs of the next
-//     item are loaded into registers while the current item computes;
-//   * staging: X to LDS as bf16 (fp32 activations: bf16 hi + lo) with the row
-//     l2 norms reduced over the lanes that hold the row, the value tile, the
-//     gates (ring g/beta for history, fused gating for the window) and their
-//     prefix sums; the window records are copied to the ring on the way
-//     (pre-mutation raw bits, single writer per qk head);
-//   * the item's checkpoint rows are then issued as non-temporal 128-bit
-//     loads (each instruction: 4 rows x 256 contiguous bytes) and stream in
-//     behind the key-side work:
-//       - Gram tiles k k^T (strictly lower) and k q^T on MFMA 16x16x32 bf16
-//         (exact products of raw bf16 keys), scaled into A and F;
-//       - M by a blocked back substitution (one window column per wave:
-//         16x16 diagonal blocks sequentially from registers, off-diagonal
-//         blocks as batched LDS reads), U and the coefficients of Z;
-//       - Z^T = C^T X and U^T V (the value part of O) on MFMA 16x16x4 fp32;
-//   * each wave finishes O for its 16 value rows: fp32 dot products of the
-//     checkpoint rows with the T columns of Z (VALU, 16-lane DPP
-//     reductions), plus the value part, scaled and stored.
+// (row, value head, value tile of BV <= 128 rows, 16 rows per wave):
+//   1. the item's checkpoint rows are issued as non-temporal 128-bit loads
+//      (lane (row c, group g) holds columns 16 i + 4 g .. +3 of row c);
+//   2. the raw keys/queries (X) and the value rows, loaded into registers
+//      while the previous item computed, are copied to LDS; the row l2 norms
+//      are reduced from the same registers; the window records are copied to
+//      the ring on the way (pre-mutation raw bits, single writer per qk head);
+//      one wave forms the gates and their prefix sums;
+//   3. Gram tiles k k^T and k q^T on MFMA 16x16x32 bf16 (exact products of raw
+//      bf16 keys) scaled into the strictly lower A (stored as one dense panel
+//      per 16-row block) and F; the next item's inputs are issued;
+//   4. M by back substitution, one window column per wave: per row one LDS
+//      read, one lane broadcast and one FMA; then U and the coefficients of Z;
+//   5. Z = C^T X on MFMA 4x4x1 (16 blocks: 64 key columns x 4 window columns
+//      per instruction, no padding at T = 4) while the other waves form the
+//      value part U^T V of their rows on the same instruction;
+//   6. S0 Z for each wave's 16 rows on MFMA 4x4x1 straight from the checkpoint
+//      registers (4 key-column groups summed by lane-half swaps), plus the
+//      value part, scaled and stored.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 struct VerifyParams {
-    int B, T, H, HV, V, L, LP, num_slots, BV, BVP, write_ring;
-    int cpv_shift;              // log2(BV / 8)
+    int B, T, H, HV, V, L, num_slots, write_ring;
+    int BV, nvt, vshift;           // value tile rows, tiles per head, log2(16-byte chunks per tile row)
     int step_vt, step_hv, step_b;  // the persistent grid stride as (vt, hv, b) digits
     float scale, softplus_threshold, eps;
     const void *q, *k, *v, *a, *b;
@@ -61,109 +60,84 @@ struct VerifyParams {
     void* o;
 };
 
-static inline int round16(int x) { return (x + 15) & ~15; }
+// Fixed workgroup: 8 waves.  Waves whose 16 value rows fall outside the tile
+// only stage data and help with the key-side work.
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
-// LDS carve-up shared by host and device.
-struct VerifyLds {
-    size_t x_hi, x_lo, rn, gam, bet, vs, us, cs, az, total;
-};
+constexpr int ilog2c(int x)
+{
+    return x <= 1 ? 0 : 1 + ilog2c(x / 2);
+}
 
-__host__ __device__ inline size_t align16(size_t x)
+constexpr size_t align16c(size_t x)
 {
     return (x + 15) & ~static_cast<size_t>(15);
 }
 
-// az holds the packed strictly-lower A during the solve, then Z^T (fp32,
-// 16 x K).
-__host__ __device__ inline VerifyLds verify_lds(int K, int LP, int BV, int BVP, int act_bytes)
-{
-    VerifyLds l;
-    const size_t KP = static_cast<size_t>(K) + 8;
-    const size_t NXR = static_cast<size_t>(LP) + 16;
-    const size_t tri = static_cast<size_t>(LP) * (LP - 1) / 2 * 4;
-    const size_t zo = 16 * static_cast<size_t>(K) * 4;
-    l.x_hi = 0;
-    l.x_lo = l.x_hi + NXR * KP * 2;
-    l.rn = l.x_lo + (act_bytes == 4 ? NXR * KP * 2 : 0);
-    l.gam = l.rn + NXR * 4;
-    l.bet = l.gam + static_cast<size_t>(LP) * 4;
-    l.vs = l.bet + static_cast<size_t>(LP) * 4;
-    l.us = l.vs + align16(static_cast<size_t>(LP) * BVP * act_bytes);
-    l.cs = l.us + static_cast<size_t>(LP + 4) * 16 * 4;
-    l.az = l.cs + (NXR + 4) * 16 * 4;
-    l.total = l.az + align16(tri > zo ? tri : zo);
-    return l;
-}
-
-// 8 consecutive activations kept as raw storage words (bit-exact for the
-// ring side channel); widened to fp32 on use.
-template <class Act>
-struct Chunk8 {
-    uint4 raw[Act::bytes / 2];
+// Compile-time layout of one instantiation: activation type, key width K,
+// ring capacity LM (64 or 128 records), value tile capacity BVM.
+template <class Act, int K_, int LM_, int BVM_>
+struct VCfg {
+    static constexpr int K = K_, LM = LM_, BVM = BVM_;
+    static constexpr int eb = Act::bytes;
+    static constexpr bool kF32 = eb == 4;
+    static constexpr int EPC = 16 / eb;            // activations per 16-byte chunk
+    static constexpr int CPR = K / EPC;            // chunks per key row
+    static constexpr int CSH = ilog2c(CPR);
+    static constexpr int KP = K + 8;               // LDS X row, bf16 elements (16-byte pad)
+    static constexpr int NXR = LM + 16;            // X rows: keys (< LM), 16 query rows at NQ0
+    static constexpr int VP = BVM + EPC;           // LDS value row, activations (16-byte pad)
+    static constexpr int FST = LM + 4;             // F / U row stride (floats)
+    static constexpr int CST = LM + 20;            // Z coefficient row stride (floats)
+    static constexpr int NBM = LM / 16;            // 16-row key blocks
+    // A is stored per 16-row block I as a dense panel of 16 rows x 16 (I + 1)
+    // columns (row stride 16 I + 20): only the part at or left of the block
+    // diagonal exists.
+    static constexpr int A_FLOATS = 128 * NBM * (NBM + 1) + 64 * NBM;
+    static constexpr int Z_FLOATS = 16 * K;
+    static constexpr int AZ = A_FLOATS > Z_FLOATS ? A_FLOATS : Z_FLOATS;
+    static constexpr int VCRM = BVM / EPC;         // chunks per value row at most
+    // register chunks per thread
+    static constexpr int MH = ((LM - 1) * CPR + kThreads - 1) / kThreads;    // history keys
+    static constexpr int MW = (2 * 16 * CPR + kThreads - 1) / kThreads;      // window keys + queries
+    static constexpr int MVH = ((LM - 1) * VCRM + kThreads - 1) / kThreads;  // history values
+    static constexpr int MVW = (16 * VCRM + kThreads - 1) / kThreads;       // window values
+    static constexpr int RPL = LM / 64;                                      // gate records per lane
+    // LDS carve-up (bytes)
+    static constexpr size_t o_xhi = 0;
+    static constexpr size_t o_xlo = o_xhi + static_cast<size_t>(NXR) * KP * 2;
+    static constexpr size_t o_v = o_xlo + (kF32 ? static_cast<size_t>(NXR) * KP * 2 : 0);
+    static constexpr size_t o_az = o_v + align16c(static_cast<size_t>(LM) * VP * eb);
+    static constexpr size_t o_fu = o_az + static_cast<size_t>(AZ) * 4;
+    static constexpr size_t o_cs = o_fu + static_cast<size_t>(16) * FST * 4;
+    static constexpr size_t o_rn = o_cs + static_cast<size_t>(16) * CST * 4;
+    static constexpr size_t o_gam = o_rn + static_cast<size_t>(NXR) * 4;
+    static constexpr size_t o_bet = o_gam + static_cast<size_t>(LM) * 4;
+    static constexpr size_t total = o_bet + static_cast<size_t>(LM) * 4;
+    // two workgroups per compute unit when they fit in 160 KB of LDS
+    static constexpr int kPerCU = total <= 80 * 1024 ? 2 : 1;
 };
 
-template <class Act>
-__device__ __forceinline__ void load8(const typename Act::storage* src, Chunk8<Act>& ch)
+// Start of block I's panel and its row stride (floats).
+__host__ __device__ constexpr int panel_base(int I)
 {
-    ch.raw[0] = *reinterpret_cast<const uint4*>(src);
-    if constexpr (Act::bytes == 4)
-        ch.raw[1] = *reinterpret_cast<const uint4*>(src + 4);
+    return 128 * I * (I + 1) + 64 * I;
 }
 
-// The chunk's 8 elements as fp32 (exact widening).
-template <class Act>
-__device__ __forceinline__ void widen8(const Chunk8<Act>& ch, float (&x)[8])
+__host__ __device__ constexpr int panel_stride(int I)
 {
-    if constexpr (Act::bytes == 2) {
-        const uint4 w = ch.raw[0];
-        x[0] = __uint_as_float(w.x << 16);
-        x[1] = __uint_as_float(w.x & 0xFFFF0000u);
-        x[2] = __uint_as_float(w.y << 16);
-        x[3] = __uint_as_float(w.y & 0xFFFF0000u);
-        x[4] = __uint_as_float(w.z << 16);
-        x[5] = __uint_as_float(w.z & 0xFFFF0000u);
-        x[6] = __uint_as_float(w.w << 16);
-        x[7] = __uint_as_float(w.w & 0xFFFF0000u);
-    } else {
-        x[0] = __uint_as_float(ch.raw[0].x);
-        x[1] = __uint_as_float(ch.raw[0].y);
-        x[2] = __uint_as_float(ch.raw[0].z);
-        x[3] = __uint_as_float(ch.raw[0].w);
-        x[4] = __uint_as_float(ch.raw[1].x);
-        x[5] = __uint_as_float(ch.raw[1].y);
-        x[6] = __uint_as_float(ch.raw[1].z);
-        x[7] = __uint_as_float(ch.raw[1].w);
-    }
+    return 16 * I + 20;
 }
 
-template <class Act>
-__device__ __forceinline__ void store8(typename Act::storage* dst, const Chunk8<Act>& ch)
-{
-    *reinterpret_cast<uint4*>(dst) = ch.raw[0];
-    if constexpr (Act::bytes == 4)
-        *reinterpret_cast<uint4*>(dst + 4) = ch.raw[1];
-}
+// e^x for the key-side coefficients as exp2 on the hardware unit: the gates'
+// prefix sums are kept pre-multiplied by log2(e).  Results below the fp32
+// normal range flush to zero.
+constexpr float kLog2e = 1.4426950408889634f;
 
-template <class Act>
-__device__ __forceinline__ void zero8(Chunk8<Act>& ch)
+__device__ __forceinline__ float exp2_hw(float x)
 {
-#pragma unroll
-    for (int i = 0; i < Act::bytes / 2; ++i)
-        ch.raw[i] = uint4{0u, 0u, 0u, 0u};
-}
-
-// Row i of a strictly lower-triangular matrix stored row by row (i >= 1).
-__host__ __device__ __forceinline__ int tri_index(int i)
-{
-    return i * (i - 1) / 2;
-}
-
-// e^x for the key-side coefficients (outputs only): exp2 of x log2(e) on the
-// hardware exp unit.  Relative error ~1e-6 for |x| <= 100; results below the
-// fp32 normal range flush to zero.
-__device__ __forceinline__ float fast_exp(float x)
-{
-    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    return __builtin_amdgcn_exp2f(x);
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane)
@@ -171,19 +145,118 @@ __device__ __forceinline__ float readlane_f(float x, int lane)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// Fixed workgroup: 8 waves.  Waves whose 16 value rows fall outside the tile
-// only stage data and help with the key-side work.
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+// x from the paired 16-lane row (16) or 32-lane half (32), added to x.  The
+// swap results are read as plain element values: a bit cast applied to an
+// element of the returned vector reads element 0 with this compiler.
+__device__ __forceinline__ float swap16_sum(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned lo = p[0], hi = p[1];
+    return __uint_as_float(lo) + __uint_as_float(hi);
+}
 
-// Staging chunks per thread, sized for rings of up to LM records.
-template <int K, int LM>
-struct StageCounts {
-    static constexpr int CPR = K / 8;                                   // chunks per X row
-    static constexpr int NXR = LM + 16;                                 // X rows at most
-    static constexpr int MXC = (NXR * CPR + kThreads - 1) / kThreads;   // X chunks / thread
-    static constexpr int MVC = (LM * 16 + kThreads - 1) / kThreads;     // V chunks / thread
-};
+__device__ __forceinline__ float swap32_sum(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned lo = p[0], hi = p[1];
+    return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+// Sum of the four 16-lane rows of a wave, delivered to every lane: rows
+// (0 + 1) and (2 + 3) by a 16-lane swap, then the two halves by a 32-lane
+// swap.  Every lane computes the same sums in the same order.
+__device__ __forceinline__ float rows4_sum(float x)
+{
+    return swap32_sum(swap16_sum(x));
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64).
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float x)
+{
+    if constexpr (W == 8) {
+        x += dpp<0xB1>(x);
+        x += dpp<0x4E>(x);
+        x += dpp<0x141>(x);
+        return x;
+    } else if constexpr (W == 16) {
+        return group16_sum(x);
+    } else if constexpr (W == 32) {
+        return swap16_sum(group16_sum(x));
+    } else {
+        return rows4_sum(group16_sum(x));
+    }
+}
+
+// Sum of squares of one 16-byte chunk of activations.
+template <class Act>
+__device__ __forceinline__ float chunk_sumsq(const uint4& w)
+{
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    float ss = 0.0f;
+    if constexpr (Act::bytes == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+            ss = __builtin_fmaf(lo, lo, ss);
+            ss = __builtin_fmaf(hi, hi, ss);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = __uint_as_float(u[e]);
+            ss = __builtin_fmaf(x, x, ss);
+        }
+    }
+    return ss;
+}
+
+// One 16-byte chunk of a key/query row into LDS: raw bf16 bits, or for fp32
+// activations the bf16 hi part and the bf16 rounding of the remainder.
+template <class Act>
+__device__ __forceinline__ void stage_x_chunk(uint16_t* hi_row, uint16_t* lo_row, const uint4& w)
+{
+    if constexpr (Act::bytes == 2) {
+        *reinterpret_cast<uint4*>(hi_row) = w;
+    } else {
+        const float x[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                            __uint_as_float(w.w)};
+        const uint32_t h0 = pack_bf16x2(x[0], x[1]), h1 = pack_bf16x2(x[2], x[3]);
+        const uint32_t l0 = pack_bf16x2(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xFFFF0000u));
+        const uint32_t l1 = pack_bf16x2(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xFFFF0000u));
+        *reinterpret_cast<uint2*>(hi_row) = uint2{h0, h1};
+        *reinterpret_cast<uint2*>(lo_row) = uint2{l0, l1};
+    }
+}
+
+// Element (row, column) of X as fp32 (hi + lo for fp32 activations).
+template <bool kF32>
+__device__ __forceinline__ float x_elem(const uint16_t* Xhi, const uint16_t* Xlo, int idx)
+{
+    float x = bf16_to_f32(Xhi[idx]);
+    if constexpr (kF32)
+        x += bf16_to_f32(Xlo[idx]);
+    return x;
+}
+
+template <class Act>
+__device__ __forceinline__ float act_f32(typename Act::storage x)
+{
+    return Act::load(&x);
+}
+
+// 16-byte load at a uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off)
+{
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+}
+
+__device__ __forceinline__ void st16(void* base, uint32_t off, const uint4& w)
+{
+    *reinterpret_cast<uint4*>(static_cast<char*>(base) + off) = w;
+}
 
 // Scalars of one work item (row b, value head hv, value tile vt).
 struct Item {
@@ -204,12 +277,12 @@ __device__ __forceinline__ void load_item_cursors(const VerifyParams& p, Item& c
 
 // The item after c in this workgroup's sequence: add the grid stride digit by
 // digit (no integer division per item).  Past the end the item is repeated.
-__device__ __forceinline__ Item next_item(const VerifyParams& p, const Item& c, int nvt)
+__device__ __forceinline__ Item next_item(const VerifyParams& p, const Item& c)
 {
     Item d = c;
     int vt = c.vt + p.step_vt, hv = c.hv + p.step_hv, b = c.b + p.step_b;
-    if (vt >= nvt) {
-        vt -= nvt;
+    if (vt >= p.nvt) {
+        vt -= p.nvt;
         ++hv;
     }
     if (hv >= p.HV) {
@@ -225,255 +298,231 @@ __device__ __forceinline__ Item next_item(const VerifyParams& p, const Item& c, 
     return d;
 }
 
-// Raw loads of one item's key-side inputs, held in registers until staged.
-template <class Act, int K, int LM>
+// Raw loads of one item's inputs, held in registers until staged.
+template <class Cfg, class Act>
 struct Prefetch {
-    using SC = StageCounts<K, LM>;
-    Chunk8<Act> xc[SC::MXC];
-    Chunk8<Act> vc[SC::MVC];
-    float rgv[2], rbv[2];
-    typename Act::storage rav[2], rbw[2];
+    uint4 xh[Cfg::MH];
+    uint4 xw[Cfg::MW];
+    uint4 vh[Cfg::MVH];
+    uint4 vw[Cfg::MVW];
+    float rg[Cfg::RPL], rb[Cfg::RPL];
+    typename Act::storage ra[Cfg::RPL], rbw[Cfg::RPL];
 };
 
-template <class Act, int K, int LM>
-__device__ __forceinline__ void issue_prefetch(const VerifyParams& p, const Item& c, int BV,
-                                               int tid, Prefetch<Act, K, LM>& f)
+template <class Cfg, class Act>
+__device__ __forceinline__ void issue_prefetch(const VerifyParams& p, const Item& c, int tid,
+                                               Prefetch<Cfg, Act>& f)
 {
     using st = typename Act::storage;
-    using SC = StageCounts<K, LM>;
-    constexpr int CPR = SC::CPR;
-    const int lane = tid & 63;
-    const int T = p.T, L = p.L;
-    const int h = c.hv / (p.HV / p.H);
-    const int NQ0 = ((c.n + 15) >> 4) << 4;
-    const st* ringk = static_cast<const st*>(p.rawk) + (static_cast<size_t>(c.s) * p.H + h) * L * K;
-    const st* ringv = static_cast<const st*>(p.rawv) + (static_cast<size_t>(c.s) * p.HV + c.hv) * L * p.V +
-                      c.vt * BV;
-    const st* kwin = static_cast<const st*>(p.k);
-    const st* qwin = static_cast<const st*>(p.q);
-    const st* vwin = static_cast<const st*>(p.v);
+    constexpr int K = Cfg::K, CPR = Cfg::CPR, CSH = Cfg::CSH, eb = Cfg::eb;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int T = p.T, L = p.L, H = p.H, HV = p.HV;
+    const int h = c.hv / (HV / H);
+    const int hist = c.hist;
+    // keys: history from the ring (qk head slab of L records), window k and q
+    const char* ringk = static_cast<const char*>(p.rawk) + (static_cast<size_t>(c.s) * H + h) * L * K * eb;
+    const char* kwin = static_cast<const char*>(p.k) + (static_cast<size_t>(c.b) * T * H + h) * K * eb;
+    const char* qwin = static_cast<const char*>(p.q) + (static_cast<size_t>(c.b) * T * H + h) * K * eb;
 #pragma unroll
-    for (int i = 0; i < SC::MXC; ++i) {
-        const int idx = i * kThreads + tid;
-        const int row = idx / CPR, ch = idx % CPR;
-        const st* src = nullptr;
-        if (row < c.hist)
-            src = ringk + static_cast<size_t>((c.base + row) & (L - 1)) * K;
-        else if (row < c.n)
-            src = kwin + ((static_cast<size_t>(c.b) * T + (row - c.hist)) * p.H + h) * K;
-        else if (row >= NQ0 && row < NQ0 + T)
-            src = qwin + ((static_cast<size_t>(c.b) * T + (row - NQ0)) * p.H + h) * K;
-        if (src)
-            load8<Act>(src + 8 * ch, f.xc[i]);
-        else
-            zero8<Act>(f.xc[i]);
+    for (int m = 0; m < Cfg::MH; ++m) {
+        const int cc = tid + kThreads * m;
+        const int row = cc >> CSH, ch = cc & (CPR - 1);
+        if (row < hist)
+            f.xh[m] = ld16(ringk, static_cast<uint32_t>(((c.base + row) & (L - 1)) * (K * eb) + ch * 16));
     }
 #pragma unroll
-    for (int i = 0; i < SC::MVC; ++i) {
-        const int idx = i * kThreads + tid;
-        const int row = idx >> p.cpv_shift, ch = idx & ((1 << p.cpv_shift) - 1);
-        if (row < c.n) {
-            const st* src = row < c.hist
-                                ? ringv + static_cast<size_t>((c.base + row) & (L - 1)) * p.V + 8 * ch
-                                : vwin + ((static_cast<size_t>(c.b) * T + (row - c.hist)) * p.HV + c.hv) *
-                                             p.V + c.vt * BV + 8 * ch;
-            load8<Act>(src, f.vc[i]);
-        } else {
-            zero8<Act>(f.vc[i]);
+    for (int m = 0; m < Cfg::MW; ++m) {
+        const int cc = tid + kThreads * m;
+        if (cc < 2 * T * CPR) {
+            const bool isq = cc >= T * CPR;
+            const int c2 = isq ? cc - T * CPR : cc;
+            const uint32_t off = static_cast<uint32_t>((c2 >> CSH) * (H * K * eb) + (c2 & (CPR - 1)) * 16);
+            f.xw[m] = ld16(isq ? qwin : kwin, off);
         }
     }
-    // gate inputs, two records per lane (wave 0 uses them); clamped addresses
-    const size_t gbase = (static_cast<size_t>(c.s) * p.HV + c.hv) * L;
+    // values: history from the ring (v head slab, this tile's columns), window v
+    const int VCR = 1 << p.vshift;
+    const size_t vrow = static_cast<size_t>(p.V) * eb;
+    const char* ringv = static_cast<const char*>(p.rawv) + (static_cast<size_t>(c.s) * HV + c.hv) * L * vrow +
+                        static_cast<size_t>(c.vt) * p.BV * eb;
+    const char* vwin = static_cast<const char*>(p.v) + (static_cast<size_t>(c.b) * T * HV + c.hv) * vrow +
+                       static_cast<size_t>(c.vt) * p.BV * eb;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int i = 2 * lane + r;
-        const int ph = (c.base + min(i, max(c.hist - 1, 0))) & (L - 1);
-        const size_t tok = static_cast<size_t>(c.b) * T + min(max(i - c.hist, 0), T - 1);
-        f.rgv[r] = p.rg[gbase + ph];
-        f.rbv[r] = p.rb[gbase + ph];
-        f.rav[r] = static_cast<const st*>(p.a)[tok * p.HV + c.hv];
-        f.rbw[r] = static_cast<const st*>(p.b)[tok * p.HV + c.hv];
+    for (int m = 0; m < Cfg::MVH; ++m) {
+        const int cc = tid + kThreads * m;
+        const int row = cc >> p.vshift, ch = cc & (VCR - 1);
+        if (row < hist)
+            f.vh[m] = ld16(ringv, static_cast<uint32_t>(((c.base + row) & (L - 1)) * vrow + ch * 16));
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::MVW; ++m) {
+        const int cc = tid + kThreads * m;
+        if (cc < T * VCR)
+            f.vw[m] = ld16(vwin, static_cast<uint32_t>((cc >> p.vshift) * (HV * vrow) + (cc & (VCR - 1)) * 16));
+    }
+    // gate inputs of records RPL lane + r (the last wave forms the gates)
+    if (wave == kWaves - 1) {
+        const size_t gbase = (static_cast<size_t>(c.s) * HV + c.hv) * L;
+#pragma unroll
+        for (int r = 0; r < Cfg::RPL; ++r) {
+            const int i = Cfg::RPL * lane + r;
+            if (i < hist) {
+                const int ph = (c.base + i) & (L - 1);
+                f.rg[r] = p.rg[gbase + ph];
+                f.rb[r] = p.rb[gbase + ph];
+            } else if (i < c.n) {
+                const size_t tok = static_cast<size_t>(c.b) * T + (i - hist);
+                f.ra[r] = static_cast<const st*>(p.a)[tok * HV + c.hv];
+                f.rbw[r] = static_cast<const st*>(p.b)[tok * HV + c.hv];
+            }
+        }
     }
 }
 
-// Diagonal 16x16 block of the unit upper-triangular solve (I + A)^T m = f
-// for rows i0..i0+15: lane j (row jrow) holds its running value in acc;
-// Ms[r] receives the solved m of row i0 + r (zero for rows at or past n).
-__device__ __forceinline__ void solve_diag_block(const float* As, int n, int i0, int jrow,
-                                                 float& acc, float (&Ms)[16])
+// Back substitution through block I of (I + A)^T m = f.  Lane j holds the
+// running value of row j (acc0: rows 0..63, acc1: rows 64..127).  Rows of
+// the block from the last: its value is final, is broadcast, and is removed
+// from every row to its left.  Lanes right of the panel are final already and
+// are left alone.
+template <int I, int LM>
+__device__ __forceinline__ void solve_block(const float* As, int lane, float& acc0, float& acc1)
 {
-    float dA[16];
+    constexpr int RS = panel_stride(I);
+    constexpr int W = 16 * (I + 1);
+    const float* pr = As + panel_base(I) + lane;
+    if constexpr (W <= 64) {
+        if (lane < W) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int i = i0 + r;
-        const bool ok = i < n && jrow >= i0 && jrow < i;
-        const float a = As[ok ? tri_index(i) + jrow : 0];
-        dA[r] = ok ? a : 0.0f;
-    }
-    const int src = i0 & 63;
+            for (int r = 15; r >= 0; --r) {
+                const float m = readlane_f(acc0, 16 * I + r);
+                acc0 = __builtin_fmaf(-pr[r * RS], m, acc0);
+            }
+        }
+    } else {
+        const bool upd1 = lane + 64 < W;
 #pragma unroll
-    for (int r = 15; r >= 0; --r) {
-        Ms[r] = readlane_f(acc, src + r);
-        acc = __builtin_fmaf(-dA[r], Ms[r], acc);
+        for (int r = 15; r >= 0; --r) {
+            const float m = readlane_f(acc1, 16 * I + r - 64);
+            acc0 = __builtin_fmaf(-pr[r * RS], m, acc0);
+            const float a1 = pr[r * RS + 64];
+            acc1 = upd1 ? __builtin_fmaf(-a1, m, acc1) : acc1;
+        }
     }
 }
 
-template <class Act, int K, int LM>
-__global__ __launch_bounds__(kThreads, 4) void verify_kernel(const VerifyParams p)
+template <int LM>
+__device__ __forceinline__ void solve_all(const float* As, int NB, int lane, float& acc0, float& acc1)
 {
+    switch (NB) {
+    case 8:
+        if constexpr (LM > 64)
+            solve_block<7, LM>(As, lane, acc0, acc1);
+        [[fallthrough]];
+    case 7:
+        if constexpr (LM > 64)
+            solve_block<6, LM>(As, lane, acc0, acc1);
+        [[fallthrough]];
+    case 6:
+        if constexpr (LM > 64)
+            solve_block<5, LM>(As, lane, acc0, acc1);
+        [[fallthrough]];
+    case 5:
+        if constexpr (LM > 64)
+            solve_block<4, LM>(As, lane, acc0, acc1);
+        [[fallthrough]];
+    case 4: solve_block<3, LM>(As, lane, acc0, acc1); [[fallthrough]];
+    case 3: solve_block<2, LM>(As, lane, acc0, acc1); [[fallthrough]];
+    case 2: solve_block<1, LM>(As, lane, acc0, acc1); [[fallthrough]];
+    case 1: solve_block<0, LM>(As, lane, acc0, acc1); [[fallthrough]];
+    default: break;
+    }
+}
+
+// The value part of the outputs for window columns 4 tg .. 4 tg + 3 on MFMA
+// 4x4x1: block (kg = lane / 16, row group) takes ring/window rows i = 4 m + kg;
+// lane l gets its 16 value rows' sums over kg's rows only.
+template <class Cfg, class Act>
+__device__ __forceinline__ f32x4 value_part(const float* FU, const typename Act::storage* Vs, int n, int tg,
+                                            int lane, int vcol)
+{
+    const int grp = lane >> 4;
+    const float* urow = FU + (4 * tg + (lane & 3)) * Cfg::FST;
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    for (int m = 0; 4 * m < n; m += 2) {
+        const int i0 = 4 * m + grp, i1 = i0 + 4;
+        const bool ok0 = i0 < n, ok1 = i1 < n;
+        const float u0 = ok0 ? urow[i0] : 0.0f, u1 = ok1 ? urow[i1] : 0.0f;
+        const float v0 = ok0 ? Act::load(Vs + i0 * Cfg::VP + vcol) : 0.0f;
+        const float v1 = ok1 ? Act::load(Vs + i1 * Cfg::VP + vcol) : 0.0f;
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u0, v0, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u1, v1, a1, 0, 0, 0);
+    }
+    return a0 + a1;
+}
+
+template <class Act, int K, int LM, int BVM, int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyParams p)
+{
+    using Cfg = VCfg<Act, K, LM, BVM>;
     using st = typename Act::storage;
-    using SC = StageCounts<K, LM>;
-    constexpr bool kF32 = Act::bytes == 4;
+    constexpr bool kF32 = Cfg::kF32;
+    constexpr int CPR = Cfg::CPR, CSH = Cfg::CSH, KP = Cfg::KP, EPC = Cfg::EPC;
+    constexpr int FST = Cfg::FST, CST = Cfg::CST, VP = Cfg::VP;
     constexpr int KS = K / 32;       // MFMA k-steps of the Gram tiles
-    constexpr int CPR = SC::CPR;
-    constexpr int KP = K + 8;        // LDS row stride of X (bf16 elements)
-    constexpr int NT = kThreads;
 
     extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* Xhi = reinterpret_cast<uint16_t*>(smem + Cfg::o_xhi);
+    uint16_t* Xlo = reinterpret_cast<uint16_t*>(smem + Cfg::o_xlo);
+    st* Vs = reinterpret_cast<st*>(smem + Cfg::o_v);
+    float* As = reinterpret_cast<float*>(smem + Cfg::o_az);   // panels of A ...
+    float* Zs = As;                                            // ... later Z [16][K]
+    float* FU = reinterpret_cast<float*>(smem + Cfg::o_fu);   // F, then U = beta M  [16][FST]
+    float* Cs = reinterpret_cast<float*>(smem + Cfg::o_cs);   // coefficients of Z   [16][CST]
+    float* rn = reinterpret_cast<float*>(smem + Cfg::o_rn);   // 1/||x|| per X row (0 on zero rows)
+    float* gam = reinterpret_cast<float*>(smem + Cfg::o_gam); // log2(e) * prefix sums of g
+    float* bet = reinterpret_cast<float*>(smem + Cfg::o_bet); // beta (0 past n)
 
-    const int BV = p.BV, nvt = p.V / BV;
-    const int nitems = p.B * p.HV * nvt;
-    const int T = p.T, L = p.L, LP = p.LP;
-    const int G = p.HV / p.H;
-
-    const VerifyLds lay = verify_lds(K, LP, BV, p.BVP, Act::bytes);
-    uint16_t* Xhi = reinterpret_cast<uint16_t*>(smem + lay.x_hi);
-    uint16_t* Xlo = reinterpret_cast<uint16_t*>(smem + lay.x_lo);
-    float* rnX = reinterpret_cast<float*>(smem + lay.rn);
-    float* gam = reinterpret_cast<float*>(smem + lay.gam);
-    float* bet = reinterpret_cast<float*>(smem + lay.bet);
-    st* Vs = reinterpret_cast<st*>(smem + lay.vs);
-    float* Us = reinterpret_cast<float*>(smem + lay.us);   // F, then U = beta M   [16][UST]
-    float* Cs = reinterpret_cast<float*>(smem + lay.cs);   // coefficients of Z    [16][CST]
-    const int UST = LP + 4, CST = LP + 16 + 4;
-    float* As = reinterpret_cast<float*>(smem + lay.az);   // packed strictly-lower A ...
-    float* Zs = reinterpret_cast<float*>(smem + lay.az);   // ... later Z^T [16][K]
+    const int nitems = p.B * p.HV * p.nvt;
+    const int T = p.T, L = p.L, G = p.HV / p.H;
+    const int TP = (T + 3) & ~3;
 
     int it = blockIdx.x;
     if (it >= nitems)
         return;
     Item cur;
-    cur.vt = it % nvt;
-    cur.hv = (it / nvt) % p.HV;
-    cur.b = it / nvt / p.HV;
+    cur.vt = it % p.nvt;
+    cur.hv = (it / p.nvt) % p.HV;
+    cur.b = it / p.nvt / p.HV;
     load_item_cursors(p, cur);
-    Prefetch<Act, K, LM> pf;
-    issue_prefetch<Act, K, LM>(p, cur, BV, threadIdx.x, pf);
+    Prefetch<Cfg, Act> pf;
+    issue_prefetch<Cfg, Act>(p, cur, threadIdx.x, pf);
 
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     for (; it < nitems; it += gridDim.x) {
-        // Per-lane indices are rederived from an opaque copy of the thread id
-        // in every iteration: kept live across the loop they would be spilled,
-        // and a spill reload waits behind the in-flight checkpoint loads.
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, wave = tid >> 6;
+        // The lane index is rebuilt in every iteration from an opaque zero
+        // (mbcnt cannot be hoisted then): a thread id kept live across the
+        // loop would be spilled, and its reload waits behind the in-flight
+        // checkpoint loads.
+        unsigned zero;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+        const int lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero)));
+        const int tid = wave * 64 + lane;
         const int col = lane & 15, grp = lane >> 4;
-        // scalars of the next item (the last item repeats itself, which keeps
-        // the prefetch below unconditional)
-        const Item nxt = next_item(p, cur, nvt);
+        // scalars of the next item (the last item repeats itself)
+        const Item nxt = next_item(p, cur);
         if (!cur.valid) {                      // padding row: nothing to read or write
-            issue_prefetch<Act, K, LM>(p, nxt, BV, tid, pf);
+            issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
             cur = nxt;
             continue;
         }
         const int s = cur.s, b = cur.b, hv = cur.hv, vt = cur.vt;
         const int h = hv / G;
         const int hist = cur.hist, n = cur.n, base = cur.base, wpc = cur.wpc;
-        const int NB = (n + 15) >> 4;   // 16-row blocks of keys
+        const int NB = (n + 15) >> 4;   // 16-row key blocks
         const int NQ0 = NB << 4;        // first query row of X
-        const int NXA = NQ0 + 16;       // X rows in use
-        const size_t gbase = (static_cast<size_t>(s) * p.HV + hv) * L;
-        st* ringk = static_cast<st*>(p.rawk) + (static_cast<size_t>(s) * p.H + h) * L * K;
-        st* ringv = static_cast<st*>(p.rawv) + (static_cast<size_t>(s) * p.HV + hv) * L * p.V + vt * BV;
+        const int BV = p.BV;
 
-        // ============ staging from the prefetch registers into LDS (raw copies)
-        const bool k_writer = p.write_ring && (hv % G == 0) && vt == 0;
-#pragma unroll
-        for (int i = 0; i < SC::MXC; ++i) {
-            const int idx = i * NT + tid;
-            const int row = idx / CPR, ch = idx % CPR;
-            if (row < NXA) {
-                if constexpr (kF32) {
-                    float xf[8];
-                    widen8<Act>(pf.xc[i], xf);
-                    uint4 hi, lo;
-                    uint32_t* hp = reinterpret_cast<uint32_t*>(&hi);
-                    uint32_t* lp = reinterpret_cast<uint32_t*>(&lo);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        hp[e] = pack_bf16x2(xf[2 * e], xf[2 * e + 1]);
-                        lp[e] = pack_bf16x2(xf[2 * e] - __uint_as_float(hp[e] << 16),
-                                            xf[2 * e + 1] - __uint_as_float(hp[e] & 0xFFFF0000u));
-                    }
-                    *reinterpret_cast<uint4*>(Xhi + row * KP + 8 * ch) = hi;
-                    *reinterpret_cast<uint4*>(Xlo + row * KP + 8 * ch) = lo;
-                } else {
-                    *reinterpret_cast<uint4*>(Xhi + row * KP + 8 * ch) = pf.xc[i].raw[0];
-                }
-                if (k_writer && row >= hist && row < n) {
-                    const int ph = (base + wpc + (row - hist)) & (L - 1);
-                    store8<Act>(ringk + static_cast<size_t>(ph) * K + 8 * ch, pf.xc[i]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < SC::MVC; ++i) {
-            const int idx = i * NT + tid;
-            const int row = idx >> p.cpv_shift, ch = idx & ((1 << p.cpv_shift) - 1);
-            if (row < n) {
-                store8<Act>(Vs + row * p.BVP + 8 * ch, pf.vc[i]);
-                if (p.write_ring && row >= hist) {
-                    const int ph = (base + wpc + (row - hist)) & (L - 1);
-                    store8<Act>(ringv + static_cast<size_t>(ph) * p.V + 8 * ch, pf.vc[i]);
-                }
-            }
-        }
-        if (wave == 0) {
-            float gl[2], bl[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int i = 2 * lane + r;
-                gl[r] = 0.0f;
-                bl[r] = 0.0f;
-                if (i < hist) {
-                    gl[r] = pf.rgv[r];
-                    bl[r] = pf.rbv[r];
-                } else if (i < n) {
-                    gdn_gate(Act::load(&pf.rav[r]), Act::load(&pf.rbw[r]), p.A_log[hv],
-                             p.dt_bias[hv], p.softplus_threshold, gl[r], bl[r]);
-                    if (p.write_ring && vt == 0) {
-                        const int ph = (base + wpc + (i - hist)) & (L - 1);
-                        p.rg[gbase + ph] = gl[r];
-                        p.rb[gbase + ph] = bl[r];
-                    }
-                }
-            }
-            // inclusive prefix sums of the gates over the combined sequence
-            const float pair = gl[0] + gl[1];
-            float incl = pair;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(incl, off, 64);
-                if (lane >= off)
-                    incl += y;
-            }
-            float excl = __shfl_up(incl, 1, 64);
-            if (lane == 0)
-                excl = 0.0f;
-            const int i0 = 2 * lane;
-            if (i0 < n) {
-                gam[i0] = excl + gl[0];
-                bet[i0] = bl[0];
-            }
-            if (i0 + 1 < n) {
-                gam[i0 + 1] = (excl + gl[0]) + gl[1];
-                bet[i0 + 1] = bl[1];
-            }
-        }
-
-        // ============ the checkpoint rows of this wave (non-temporal stream):
-        // lane (row col, group grp) holds columns 16 i + 4 grp .. +3 of row
-        // r0 + col, the fp32 MFMA operand order (k step 4 i + e).
+        // ============ 1. checkpoint rows of this wave (non-temporal stream)
         const bool has_rows = wave * 16 < BV;
         const int r0 = vt * BV + (has_rows ? wave * 16 : 0);
         const float* Srow = p.S + ((static_cast<size_t>(s) * p.HV + hv) * p.V + r0 + col) * K + 4 * grp;
@@ -481,213 +530,261 @@ __global__ __launch_bounds__(kThreads, 4) void verify_kernel(const VerifyParams 
 #pragma unroll
         for (int i = 0; i < K / 16; ++i)
             sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + 16 * i));
-        __syncthreads();
 
-        // ============ l2 norms of the X rows: 16 lanes per row from LDS.  For
-        // fp32 activations the row is the staged hi + lo pair.
-        for (int row0 = 0; row0 < NXA; row0 += 4 * kWaves) {
-            const int row = row0 + 4 * wave + grp;
+        // ============ 2. staging from the prefetch registers
+        const bool write_ring = p.write_ring != 0;
+        const bool k_writer = write_ring && (hv % G == 0) && vt == 0;
+        char* ringk = static_cast<char*>(p.rawk) + (static_cast<size_t>(s) * p.H + h) * L * K * Cfg::eb;
+        // history keys
+#pragma unroll
+        for (int m = 0; m < Cfg::MH; ++m) {
+            const int cc = tid + kThreads * m;
+            const int row = cc >> CSH, ch = cc & (CPR - 1);
             float ss = 0.0f;
-            if (row < NXA) {
+            if (row < hist) {
+                stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xh[m]);
+                ss = chunk_sumsq<Act>(pf.xh[m]);
+            }
+            ss = lane_group_sum<CPR>(ss);
+            if (row < hist && ch == 0)
+                rn[row] = 1.0f / sqrtf(ss + p.eps);
+        }
+        // window keys (rows hist..n-1) and queries (rows NQ0..NQ0+T-1)
 #pragma unroll
-                for (int m = 0; m < K / 128; ++m) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(Xhi + row * KP + 128 * m + 8 * col);
-                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-                    uint32_t wl[4] = {0u, 0u, 0u, 0u};
-                    if constexpr (kF32) {
-                        const uint4 l = *reinterpret_cast<const uint4*>(Xlo + row * KP + 128 * m + 8 * col);
-                        wl[0] = l.x; wl[1] = l.y; wl[2] = l.z; wl[3] = l.w;
-                    }
+        for (int m = 0; m < Cfg::MW; ++m) {
+            const int cc = tid + kThreads * m;
+            const bool live = cc < 2 * T * CPR;
+            const bool isq = cc >= T * CPR;
+            const int c2 = isq ? cc - T * CPR : cc;
+            const int t = c2 >> CSH, ch = c2 & (CPR - 1);
+            const int row = isq ? NQ0 + t : hist + t;
+            float ss = 0.0f;
+            if (live) {
+                stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xw[m]);
+                ss = chunk_sumsq<Act>(pf.xw[m]);
+                if (!isq && k_writer)
+                    st16(ringk, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * (K * Cfg::eb) + ch * 16),
+                         pf.xw[m]);
+            }
+            ss = lane_group_sum<CPR>(ss);
+            if (live && ch == 0)
+                rn[row] = 1.0f / sqrtf(ss + p.eps);
+        }
+        // key rows n..NQ0-1 are zero (they pad the last Gram block)
+        for (int cc = tid; cc < (NQ0 - n) * CPR; cc += kThreads) {
+            const int row = n + (cc >> CSH), ch = cc & (CPR - 1);
+            const uint4 z = {0u, 0u, 0u, 0u};
+            stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, z);
+            if (ch == 0)
+                rn[row] = 0.0f;
+        }
+        // value rows of the tile
+        {
+            const int VCR = 1 << p.vshift;
+            const size_t vrow = static_cast<size_t>(p.V) * Cfg::eb;
+            char* ringv = static_cast<char*>(p.rawv) + (static_cast<size_t>(s) * p.HV + hv) * L * vrow +
+                          static_cast<size_t>(vt) * BV * Cfg::eb;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x0 = __uint_as_float(ww[e] << 16) + __uint_as_float(wl[e] << 16);
-                        const float x1 = __uint_as_float(ww[e] & 0xFFFF0000u) +
-                                         __uint_as_float(wl[e] & 0xFFFF0000u);
-                        ss = __builtin_fmaf(x0, x0, ss);
-                        ss = __builtin_fmaf(x1, x1, ss);
-                    }
-                }
-                if constexpr (K == 64) {
-                    // 64 columns over 16 lanes: 4 per lane
-                    ss = 0.0f;
-                    const uint2 w = *reinterpret_cast<const uint2*>(Xhi + row * KP + 4 * col);
-                    uint2 l = {0u, 0u};
-                    if constexpr (kF32)
-                        l = *reinterpret_cast<const uint2*>(Xlo + row * KP + 4 * col);
-                    const uint32_t ww[2] = {w.x, w.y}, wl[2] = {l.x, l.y};
+            for (int m = 0; m < Cfg::MVH; ++m) {
+                const int cc = tid + kThreads * m;
+                const int row = cc >> p.vshift, ch = cc & (VCR - 1);
+                if (row < hist)
+                    *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = pf.vh[m];
+            }
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float x0 = __uint_as_float(ww[e] << 16) + __uint_as_float(wl[e] << 16);
-                        const float x1 = __uint_as_float(ww[e] & 0xFFFF0000u) +
-                                         __uint_as_float(wl[e] & 0xFFFF0000u);
-                        ss = __builtin_fmaf(x0, x0, ss);
-                        ss = __builtin_fmaf(x1, x1, ss);
-                    }
+            for (int m = 0; m < Cfg::MVW; ++m) {
+                const int cc = tid + kThreads * m;
+                if (cc < T * VCR) {
+                    const int t = cc >> p.vshift, ch = cc & (VCR - 1);
+                    *reinterpret_cast<uint4*>(Vs + (hist + t) * VP + ch * EPC) = pf.vw[m];
+                    if (write_ring)
+                        st16(ringv, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * vrow + ch * 16), pf.vw[m]);
                 }
             }
-            ss = group16_sum(ss);
-            if (row < NXA && col == 0) {
-                const bool real = row < n || (row >= NQ0 && row < NQ0 + T);
-                rnX[row] = real ? 1.0f / sqrtf(ss + p.eps) : 0.0f;
+        }
+        // gates of the combined sequence and their prefix sums (last wave)
+        if (wave == kWaves - 1) {
+            const size_t gbase = (static_cast<size_t>(s) * p.HV + hv) * L;
+            float gl[Cfg::RPL], bl[Cfg::RPL];
+            float pair = 0.0f;
+#pragma unroll
+            for (int r = 0; r < Cfg::RPL; ++r) {
+                const int i = Cfg::RPL * lane + r;
+                gl[r] = 0.0f;
+                bl[r] = 0.0f;
+                if (i < hist) {
+                    gl[r] = pf.rg[r];
+                    bl[r] = pf.rb[r];
+                } else if (i < n) {
+                    gdn_gate(act_f32<Act>(pf.ra[r]), act_f32<Act>(pf.rbw[r]), p.A_log[hv], p.dt_bias[hv],
+                             p.softplus_threshold, gl[r], bl[r]);
+                    if (write_ring && vt == 0) {
+                        const int ph = (base + wpc + (i - hist)) & (L - 1);
+                        p.rg[gbase + ph] = gl[r];
+                        p.rb[gbase + ph] = bl[r];
+                    }
+                }
+                pair += gl[r];
+            }
+            float incl = pair;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(incl, off, 64);
+                if (lane >= off)
+                    incl += y;
+            }
+            float run = __shfl_up(incl, 1, 64);
+            if (lane == 0)
+                run = 0.0f;
+#pragma unroll
+            for (int r = 0; r < Cfg::RPL; ++r) {
+                const int i = Cfg::RPL * lane + r;
+                run += gl[r];
+                gam[i] = run * kLog2e;
+                bet[i] = bl[r];
             }
         }
         __syncthreads();
 
-        // ============ Gram tiles: A (strictly lower, n x n) and F (n x T)
-        const int NT1 = NB * (NB + 1) / 2;
-        for (int ti = wave; ti < NT1 + NB; ti += kWaves) {
-            int I, rowJ;
-            const bool qtile = ti >= NT1;
-            if (!qtile) {
-                I = 0;
-                while ((I + 1) * (I + 2) / 2 <= ti)
-                    ++I;
-                rowJ = 16 * (ti - I * (I + 1) / 2);
-            } else {
-                I = ti - NT1;
-                rowJ = NQ0;
-            }
+        // ============ 3. Gram tiles.  Block row I holds I + 1 tiles of A
+        // (J <= I) and one tile of F (its keys against the queries).
+        const int ntiles = NB * (NB + 3) / 2;
+        for (int ti = wave; ti < ntiles; ti += kWaves) {
+            int I = 0;
+            while ((I + 1) * (I + 4) / 2 <= ti)
+                ++I;
+            const int J = ti - I * (I + 3) / 2;
+            const bool ftile = J == I + 1;
+            const int rowA = 16 * (ftile ? I : J) + col;   // MFMA rows m: keys j
+            const int rowB = (ftile ? NQ0 : 16 * I) + col; // MFMA columns n: keys i or queries t
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = 32 * ks + 8 * grp;
-                const bf16x8 xa = *reinterpret_cast<const bf16x8*>(Xhi + (16 * I + col) * KP + off);
-                const bf16x8 xb = *reinterpret_cast<const bf16x8*>(Xhi + (rowJ + col) * KP + off);
+                const bf16x8 xa = *reinterpret_cast<const bf16x8*>(Xhi + rowA * KP + off);
+                const bf16x8 xb = *reinterpret_cast<const bf16x8*>(Xhi + rowB * KP + off);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xb, acc, 0, 0, 0);
                 if constexpr (kF32) {
-                    const bf16x8 la = *reinterpret_cast<const bf16x8*>(Xlo + (16 * I + col) * KP + off);
-                    const bf16x8 lb = *reinterpret_cast<const bf16x8*>(Xlo + (rowJ + col) * KP + off);
+                    const bf16x8 la = *reinterpret_cast<const bf16x8*>(Xlo + rowA * KP + off);
+                    const bf16x8 lb = *reinterpret_cast<const bf16x8*>(Xlo + rowB * KP + off);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, lb, acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la, xb, acc, 0, 0, 0);
                 }
             }
+            // lane (col, grp) holds rows j = 16 (I or J) + 4 grp + jj of column col
+            const int j4 = rowA - col + 4 * grp;
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(gam + j4);
+            const f32x4 rj = *reinterpret_cast<const f32x4*>(rn + j4);
+            f32x4 val;
+            if (!ftile) {
+                const int i = 16 * I + col;
+                const float gi = gam[i], bri = bet[i] * rn[i];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * I + 4 * grp + jj;
-                if (!qtile) {
-                    const int j = rowJ + col;
-                    if (j < i && i < n)
-                        As[tri_index(i) + j] = bet[i] * fast_exp(gam[i] - gam[j]) * rnX[i] * rnX[j] * acc[jj];
-                } else {
-                    const int t = col;
-                    float val = 0.0f;
-                    if (t < T && i < n && i <= hist + t)
-                        val = fast_exp(gam[min(hist + t, n - 1)] - gam[i]) * rnX[i] * rnX[NQ0 + t] * acc[jj];
-                    Us[t * UST + i] = val;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float x = acc[jj] * bri * rj[jj] * exp2_hw(gi - gj[jj]);
+                    val[jj] = (J == I && 4 * grp + jj >= col) ? 0.0f : x;
                 }
+                *reinterpret_cast<f32x4*>(As + panel_base(I) + col * panel_stride(I) + 16 * J + 4 * grp) = val;
+            } else {
+                const int t = col;
+                const int tc = t < T ? t : T - 1;
+                const int ht = hist + tc;
+                const float gq = gam[ht], rq = rn[NQ0 + tc];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float x = acc[jj] * rq * rj[jj] * exp2_hw(gq - gj[jj]);
+                    val[jj] = (t < T && j4 + jj <= ht) ? x : 0.0f;
+                }
+                *reinterpret_cast<f32x4*>(FU + t * FST + j4) = val;
             }
         }
-        // coefficient rows of Z that no solve column writes: zero
-        for (int idx = tid; idx < NXA * 16; idx += NT) {
-            const int t = idx / NXA, row = idx - t * NXA;
-            if (row >= n || t >= T)
-                Cs[t * CST + row] = 0.0f;
-        }
-        // the next item's key-side inputs stream in behind the rest of this one
-        issue_prefetch<Act, K, LM>(p, nxt, BV, tid, pf);
+        // the next item's inputs stream in behind the rest of this one
+        issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
         __syncthreads();
 
-        // ============ M = (I + A)^{-T} F, one window column per wave.  Lane j
-        // holds row j (acc0) and row j+64 (acc1).  Blocks of 16 rows from the
-        // last: the diagonal block is solved sequentially from registers, then
-        // its solution updates all earlier rows at once.  Rows at or past n
-        // carry zero coefficients, so their M stays zero and no step branches.
-        for (int t = wave; t < T; t += kWaves) {
-            const float f0 = Us[t * UST + lane];                  // F
-            const float f1 = LM > 64 ? Us[t * UST + 64 + lane] : 0.0f;
-            float acc0 = lane < n ? f0 : 0.0f;
-            float acc1 = lane + 64 < n ? f1 : 0.0f;
-            for (int I = NB - 1; I >= 0; --I) {
-                const int i0 = 16 * I;
-                float Ms[16];
-                if (LM <= 64 || i0 < 64)
-                    solve_diag_block(As, n, i0, lane, acc0, Ms);
-                else
-                    solve_diag_block(As, n, i0, lane + 64, acc1, Ms);
+        // ============ 4. M = (I + A)^{-T} F, one window column per wave
+        for (int t = wave; t < TP; t += kWaves) {
+            float acc0 = FU[t * FST + lane];
+            float acc1 = LM > 64 ? FU[t * FST + 64 + lane] : 0.0f;
+            solve_all<LM>(As, NB, lane, acc0, acc1);
+            // U = beta M; Z coefficients -beta e^{Gam} rn M on keys
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = i0 + r;
-                    const int tri = tri_index(min(i, n - 1));
-                    const float a0 = As[tri + min(lane, i0 > 0 ? i0 - 1 : 0)];
-                    acc0 = __builtin_fmaf(-((lane < i0 && i < n) ? a0 : 0.0f), Ms[r], acc0);
-                    if (LM > 64) {
-                        const int j1 = lane + 64;
-                        const float a1 = As[tri + min(j1, i0 > 0 ? i0 - 1 : 0)];
-                        acc1 = __builtin_fmaf(-((j1 < i0 && i < n) ? a1 : 0.0f), Ms[r], acc1);
-                    }
-                }
-            }
-            // U = beta M; Z coefficients: -beta e^{Gam} rn M on keys, e^{Gam_win} rn_q on the query
-#pragma unroll
-            for (int hh = 0; hh < (LM > 64 ? 2 : 1); ++hh) {
+            for (int hh = 0; hh < LM / 64; ++hh) {
                 const int j = lane + 64 * hh;
                 const float m = hh ? acc1 : acc0;
-                if (j < n) {
-                    Us[t * UST + j] = bet[j] * m;
-                    Cs[t * CST + j] = -bet[j] * fast_exp(gam[j]) * rnX[j] * m;
-                }
+                const bool ok = j < n;
+                const float bj = bet[j];
+                const float u = bj * m;
+                const float cf = -(bj * rn[j]) * exp2_hw(gam[j]) * m;
+                FU[t * FST + j] = ok ? u : 0.0f;
+                Cs[t * CST + j] = ok ? cf : 0.0f;
             }
-            if (lane < 16)
-                Cs[t * CST + NQ0 + lane] = lane == t ? fast_exp(gam[hist + t]) * rnX[NQ0 + t] : 0.0f;
         }
         __syncthreads();
 
-        // ============ Z^T = C^T X: 16-wide k tiles over the waves, two
-        // interleaved accumulators.
-        for (int kt = wave; kt < K / 16; kt += kWaves) {
+        // ============ 5. Z = C^T X (keys) + the query terms, on MFMA 4x4x1:
+        // unit (tg, kset): window columns 4 tg .. +3, key columns 64 kset + lane.
+        constexpr int NKS = K / 64;
+        for (int u = wave; u < (TP / 4) * NKS; u += kWaves) {
+            const int tg = u / NKS, ks = u % NKS;
+            const float* crow = Cs + (4 * tg + (lane & 3)) * CST;
+            const int kc = 64 * ks + lane;
             f32x4 z0 = {0.0f, 0.0f, 0.0f, 0.0f}, z1 = z0;
-            for (int q = 0; q < NXA / 4; q += 2) {
-                const int i = 4 * q + grp;
-                float x0 = bf16_to_f32(Xhi[i * KP + 16 * kt + col]);
-                float x1 = bf16_to_f32(Xhi[(i + 4) * KP + 16 * kt + col]);
-                if constexpr (kF32) {
-                    x0 += bf16_to_f32(Xlo[i * KP + 16 * kt + col]);
-                    x1 += bf16_to_f32(Xlo[(i + 4) * KP + 16 * kt + col]);
-                }
-                z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Cs[col * CST + i], x0, z0, 0, 0, 0);
-                z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Cs[col * CST + i + 4], x1, z1, 0, 0, 0);
+            for (int i = 0; i < n; i += 4) {
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(crow + i);
+                const float x0 = x_elem<kF32>(Xhi, Xlo, (i + 0) * KP + kc);
+                const float x1 = x_elem<kF32>(Xhi, Xlo, (i + 1) * KP + kc);
+                const float x2 = x_elem<kF32>(Xhi, Xlo, (i + 2) * KP + kc);
+                const float x3 = x_elem<kF32>(Xhi, Xlo, (i + 3) * KP + kc);
+                z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[0], x0, z0, 0, 0, 0);
+                z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[1], x1, z1, 0, 0, 0);
+                z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[2], x2, z0, 0, 0, 0);
+                z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[3], x3, z1, 0, 0, 0);
             }
-            // lane (k = 16 kt + col, rows t = 4 grp + jj)
+            // lane l, register r: Z[4 tg + r][kc]; add e^{Gam_{h+t}} rn_q q_t
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                Zs[(4 * grp + jj) * K + 16 * kt + col] = z0[jj] + z1[jj];
-        }
-        // the value part U^T V of this wave's 16 rows, in the output layout:
-        // lane (row col, window positions t = 4 grp + jj)
-        f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = o0;
-        if (has_rows) {
-            for (int q = 0; q < (n + 3) / 4; q += 2) {
-                const int i = 4 * q + grp;
-                const bool ok0 = i < n, ok1 = i + 4 < n;
-                const float v0 = ok0 ? Act::load(Vs + i * p.BVP + wave * 16 + col) : 0.0f;
-                const float v1 = ok1 ? Act::load(Vs + (i + 4) * p.BVP + wave * 16 + col) : 0.0f;
-                const float u0 = ok0 ? Us[col * UST + i] : 0.0f;
-                const float u1 = ok1 ? Us[col * UST + i + 4] : 0.0f;
-                o0 = __builtin_amdgcn_mfma_f32_16x16x4f32(u0, v0, o0, 0, 0, 0);
-                o1 = __builtin_amdgcn_mfma_f32_16x16x4f32(u1, v1, o1, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * tg + r;
+                float z = z0[r] + z1[r];
+                if (t < T) {
+                    const float cq = exp2_hw(gam[hist + t]) * rn[NQ0 + t];
+                    z = __builtin_fmaf(cq, x_elem<kF32>(Xhi, Xlo, (NQ0 + t) * KP + kc), z);
+                }
+                Zs[t * K + kc] = z;
             }
         }
+        // the value part of this wave's rows for the first four window columns
+        const int vcol = wave * 16 + col;
+        f32x4 vp0 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (has_rows)
+            vp0 = value_part<Cfg, Act>(FU, Vs, n, 0, lane, vcol);
         __syncthreads();
 
-        // ============ O = S0 Z + V^T U for this wave's 16 rows on fp32 MFMA:
-        // A = Z^T (lane (t col, group grp) reads Z[t][16 i + 4 grp + e]),
-        // B = the checkpoint registers, accumulators seeded with the value part.
+        // ============ 6. O = S0 Z + V^T U for this wave's 16 rows.  Block
+        // (kg = grp, rows 4 (col / 4) .. +3) sums key columns 16 i + 4 kg + e;
+        // the four kg partial sums meet by lane swaps.
         if (has_rows) {
-#pragma unroll
-            for (int i = 0; i < K / 16; ++i) {
-                const f32x4 za = *reinterpret_cast<const f32x4*>(Zs + col * K + 16 * i + 4 * grp);
-                f32x4& acc = (i & 1) ? o1 : o0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(za[e], sraw[i][e], acc, 0, 0, 0);
-            }
             st* out = static_cast<st*>(p.o);
+            for (int tg = 0; tg < TP / 4; ++tg) {
+                f32x4 a0 = tg == 0 ? vp0 : value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol);
+                f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float* zrow = Zs + (4 * tg + (lane & 3)) * K + 4 * grp;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int t = 4 * grp + jj;
+                for (int i = 0; i < K / 16; ++i) {
+                    const f32x4 za = *reinterpret_cast<const f32x4*>(zrow + 16 * i);
+                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], a1, 0, 0, 0);
+                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], a1, 0, 0, 0);
+                }
+                const f32x4 tot = a0 + a1;
+                const float o0 = rows4_sum(tot[0]), o1 = rows4_sum(tot[1]);
+                const float o2 = rows4_sum(tot[2]), o3 = rows4_sum(tot[3]);
+                const float val = grp == 0 ? o0 : grp == 1 ? o1 : grp == 2 ? o2 : o3;
+                const int t = 4 * tg + grp;
                 if (t < T)
                     out[((static_cast<size_t>(b) * T + t) * p.HV + hv) * p.V + r0 + col] =
-                        Act::from_f32(p.scale * (o0[jj] + o1[jj]));
+                        Act::from_f32(p.scale * val);
             }
         }
         __syncthreads();   // LDS is restaged by the next item
@@ -697,25 +794,61 @@ __global__ __launch_bounds__(kThreads, 4) void verify_kernel(const VerifyParams 
 
 // ------------------------------------------------------------------- host
 
-// Value rows per work item: the largest power of two (16..128) that divides V,
-// 16 per wave.
+template <class Act, int K, int LM>
+struct VSel;
+
+// Value tile capacity per instantiation: 128 rows, except fp32 activations
+// with 128-record rings (32 rows) where LDS would not hold more.
+template <class Act, int LM>
+constexpr int bvm_of()
+{
+    return (Act::bytes == 4 && LM > 64) ? 32 : 128;
+}
+
+template <class Act, int K, int LM>
+using CfgOf = VCfg<Act, K, LM, bvm_of<Act, LM>()>;
+
+template <class Act, int K, int LM>
+static size_t lds_of()
+{
+    return CfgOf<Act, K, LM>::total;
+}
+
+static size_t lds_for(const gdn_shape& sh)
+{
+    const bool bf = sh.act == GDN_BF16;
+    const bool big = sh.L > 64;
+    switch (sh.K) {
+    case 64:
+        return bf ? (big ? lds_of<ActBF16, 64, 128>() : lds_of<ActBF16, 64, 64>())
+                  : (big ? lds_of<ActF32, 64, 128>() : lds_of<ActF32, 64, 64>());
+    case 128:
+        return bf ? (big ? lds_of<ActBF16, 128, 128>() : lds_of<ActBF16, 128, 64>())
+                  : (big ? lds_of<ActF32, 128, 128>() : lds_of<ActF32, 128, 64>());
+    case 256:
+        return bf ? lds_of<ActBF16, 256, 64>() : lds_of<ActF32, 256, 64>();
+    default: return ~static_cast<size_t>(0);
+    }
+}
+
+static int bvm_for(const gdn_shape& sh)
+{
+    return (sh.act == GDN_F32 && sh.L > 64) ? 32 : 128;
+}
+
+// Value rows per work item: the largest power of two (16..capacity) that
+// divides V, 16 per wave.
 int verify_tile_cols(const gdn_shape& sh)
 {
-    for (int bv = 16 * kWaves; bv >= 16; bv >>= 1)
+    for (int bv = bvm_for(sh); bv >= 16; bv >>= 1)
         if (sh.V % bv == 0)
             return bv;
     return 16;
 }
 
-static int verify_bvp(const gdn_shape& sh)
-{
-    return verify_tile_cols(sh) + 8;
-}
-
 size_t verify_lds_bytes(const gdn_shape& sh)
 {
-    const int LP = round16(sh.L);
-    return verify_lds(sh.K, LP, verify_tile_cols(sh), verify_bvp(sh), sh.act == GDN_BF16 ? 2 : 4).total;
+    return lds_for(sh);
 }
 
 size_t max_lds_bytes()
@@ -742,8 +875,10 @@ static int compute_units()
 template <class Act, int K, int LM>
 static hipError_t launch_verify_k(const gdn_shape& sh, const VerifyParams& p, hipStream_t stream)
 {
-    const size_t lds = verify_lds_bytes(sh);
-    auto kern = verify_kernel<Act, K, LM>;
+    using Cfg = CfgOf<Act, K, LM>;
+    constexpr int kMinWaves = Cfg::kPerCU == 2 ? 4 : 2;
+    const size_t lds = Cfg::total;
+    auto kern = verify_kernel<Act, K, LM, Cfg::BVM, kMinWaves>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -751,15 +886,14 @@ static hipError_t launch_verify_k(const gdn_shape& sh, const VerifyParams& p, hi
         if (e != hipSuccess)
             return e;
     }
-    // persistent grid: two workgroups per compute unit, never more than items
-    const int nvt = sh.V / p.BV;
-    const long long items = static_cast<long long>(sh.B) * sh.HV * nvt;
-    const long long cap = 2LL * compute_units();
+    // persistent grid: as many workgroups as fit at once, never more than items
+    const long long items = static_cast<long long>(sh.B) * sh.HV * p.nvt;
+    const long long cap = static_cast<long long>(Cfg::kPerCU) * compute_units();
     const unsigned grid = static_cast<unsigned>(items < cap ? items : cap);
     VerifyParams q = p;
-    q.step_vt = static_cast<int>(grid % nvt);
-    q.step_hv = static_cast<int>((grid / nvt) % sh.HV);
-    q.step_b = static_cast<int>(grid / nvt / sh.HV);
+    q.step_vt = static_cast<int>(grid % p.nvt);
+    q.step_hv = static_cast<int>((grid / p.nvt) % sh.HV);
+    q.step_b = static_cast<int>(grid / p.nvt / sh.HV);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, q);
     return hipGetLastError();
 }
@@ -798,14 +932,15 @@ hipError_t launch_verify(const gdn_shape& sh, const WindowPtrs& w, const float* 
     p.HV = sh.HV;
     p.V = sh.V;
     p.L = sh.L;
-    p.LP = round16(sh.L);
     p.num_slots = sh.num_slots;
-    p.BV = verify_tile_cols(sh);
-    p.cpv_shift = 0;
-    while ((8 << p.cpv_shift) < p.BV)
-        ++p.cpv_shift;
-    p.BVP = verify_bvp(sh);
     p.write_ring = write_ring;
+    p.BV = verify_tile_cols(sh);
+    p.nvt = sh.V / p.BV;
+    const int eb = sh.act == GDN_BF16 ? 2 : 4;
+    const int vcr = p.BV * eb / 16;      // 16-byte chunks per value-tile row (power of two)
+    p.vshift = 0;
+    while ((1 << p.vshift) < vcr)
+        ++p.vshift;
     p.scale = sh.scale;
     p.softplus_threshold = sh.softplus_threshold;
     p.eps = sh.l2norm_eps;
