@@ -21,7 +21,8 @@
 // Execution: a persistent grid; each workgroup (8 waves) strides over items
 // (row, value head, value tile of BV <= 128 rows, 16 rows per wave):
 //   1. the item's checkpoint rows are issued as non-temporal 128-bit loads
-//      (lane (row c, group g) holds columns 16 i + 4 g .. +3 of row c);
+//      (lane (row c, group g) holds columns 16 i + 4 g .. +3 of row c), in
+//      four groups at the first four phase boundaries (a steady stream);
 //   2. the raw keys/queries (X) and the value rows, loaded into registers
 //      while the previous item computed, are copied to LDS; the row l2 norms
 //      are reduced from the same registers; the window records are copied to
@@ -172,6 +173,28 @@ __device__ __forceinline__ float rows4_sum(float x)
     return swap32_sum(swap16_sum(x));
 }
 
+// DPP move of x with row mask RM; lanes without a source (or outside the
+// mask) receive 0.
+template <int CTRL, int RM>
+__device__ __forceinline__ float dpp0(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, RM, 0xF, true));
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the last lane of row 0 into row 1 (and of row 2 into row
+// 3) and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ float wave_incl_scan(float x)
+{
+    x += dpp0<0x111, 0xF>(x);   // row_shr:1
+    x += dpp0<0x112, 0xF>(x);   // row_shr:2
+    x += dpp0<0x114, 0xF>(x);   // row_shr:4
+    x += dpp0<0x118, 0xF>(x);   // row_shr:8
+    x += dpp0<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp0<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 // Sum over aligned groups of W lanes (W = 8, 16, 32 or 64).
 template <int W>
 __device__ __forceinline__ float lane_group_sum(float x)
@@ -190,7 +213,8 @@ __device__ __forceinline__ float lane_group_sum(float x)
     }
 }
 
-// Sum of squares of one 16-byte chunk of activations.
+// Sum of squares of one 16-byte chunk of activations (bf16 pairs on the
+// packed dot-product unit: exact products, fp32 sums).
 template <class Act>
 __device__ __forceinline__ float chunk_sumsq(const uint4& w)
 {
@@ -199,9 +223,9 @@ __device__ __forceinline__ float chunk_sumsq(const uint4& w)
     if constexpr (Act::bytes == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
-            ss = __builtin_fmaf(lo, lo, ss);
-            ss = __builtin_fmaf(hi, hi, ss);
+            const uint32_t ue = u[e];
+            const bf16x2 x = __builtin_bit_cast(bf16x2, ue);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
         }
     } else {
 #pragma unroll
@@ -211,6 +235,12 @@ __device__ __forceinline__ float chunk_sumsq(const uint4& w)
         }
     }
     return ss;
+}
+
+// 1 / sqrt(ss + eps) on the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rnorm_hw(float ss, float eps)
+{
+    return __builtin_amdgcn_rsqf(ss + eps);
 }
 
 // One 16-byte chunk of a key/query row into LDS: raw bf16 bits, or for fp32
@@ -241,10 +271,15 @@ __device__ __forceinline__ float x_elem(const uint16_t* Xhi, const uint16_t* Xlo
     return x;
 }
 
+// Activation element idx from the aligned 32-bit word that holds it (exact
+// widening).
 template <class Act>
-__device__ __forceinline__ float act_f32(typename Act::storage x)
+__device__ __forceinline__ float act_from_word(uint32_t w, size_t idx)
 {
-    return Act::load(&x);
+    if constexpr (Act::bytes == 2)
+        return __uint_as_float((idx & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    else
+        return __uint_as_float(w);
 }
 
 // 16-byte load at a uniform base plus a 32-bit per-lane byte offset.
@@ -258,6 +293,16 @@ __device__ __forceinline__ void st16(void* base, uint32_t off, const uint4& w)
     *reinterpret_cast<uint4*>(static_cast<char*>(base) + off) = w;
 }
 
+// Read-only, wave-uniform metadata (slot indices, cursors, gate parameters)
+// through the constant address space: scalar loads, counted apart from the
+// vector loads, so reading them never waits on the checkpoint stream.
+template <class T>
+__device__ __forceinline__ T ld_uniform(const T* ptr, size_t i)
+{
+    typedef const __attribute__((address_space(4))) T* cptr;
+    return ((cptr)ptr)[i];
+}
+
 // Scalars of one work item (row b, value head hv, value tile vt).
 struct Item {
     int valid, s, b, hv, vt, hist, n, base, wpc;
@@ -265,12 +310,12 @@ struct Item {
 
 __device__ __forceinline__ void load_item_cursors(const VerifyParams& p, Item& c)
 {
-    const int s = p.slot_idx[c.b];
+    const int s = ld_uniform(p.slot_idx, c.b);
     c.valid = valid_slot(s, p.num_slots);
     c.s = c.valid ? s : 0;            // padding rows address slot 0 but never use it
-    const bool flagged = p.is_flush[c.s] != 0;
-    c.wpc = clamp_wp(p.write_pos[c.s], p.L, p.T);
-    c.base = p.cache_base[c.s];
+    const bool flagged = ld_uniform(p.is_flush, c.s) != 0;
+    c.wpc = clamp_wp(ld_uniform(p.write_pos, c.s), p.L, p.T);
+    c.base = ld_uniform(p.cache_base, c.s);
     c.hist = flagged ? 0 : c.wpc;
     c.n = c.hist + p.T;
 }
@@ -306,7 +351,7 @@ struct Prefetch {
     uint4 vh[Cfg::MVH];
     uint4 vw[Cfg::MVW];
     float rg[Cfg::RPL], rb[Cfg::RPL];
-    typename Act::storage ra[Cfg::RPL], rbw[Cfg::RPL];
+    uint32_t ra[Cfg::RPL], rbw[Cfg::RPL];   // aligned 32-bit words holding the activations
 };
 
 template <class Cfg, class Act>
@@ -360,23 +405,38 @@ __device__ __forceinline__ void issue_prefetch(const VerifyParams& p, const Item
         if (cc < T * VCR)
             f.vw[m] = ld16(vwin, static_cast<uint32_t>((cc >> p.vshift) * (HV * vrow) + (cc & (VCR - 1)) * 16));
     }
-    // gate inputs of records RPL lane + r (the last wave forms the gates)
+    // gate inputs of records RPL lane + r (the last wave forms the gates):
+    // every lane loads all four, at clamped in-range indices, so no load is
+    // conditional (a register written by a load on one path and a copy on
+    // the other would have to wait for the load)
     if (wave == kWaves - 1) {
         const size_t gbase = (static_cast<size_t>(c.s) * HV + c.hv) * L;
+        const int hl = hist > 0 ? hist - 1 : 0;
 #pragma unroll
         for (int r = 0; r < Cfg::RPL; ++r) {
             const int i = Cfg::RPL * lane + r;
-            if (i < hist) {
-                const int ph = (c.base + i) & (L - 1);
-                f.rg[r] = p.rg[gbase + ph];
-                f.rb[r] = p.rb[gbase + ph];
-            } else if (i < c.n) {
-                const size_t tok = static_cast<size_t>(c.b) * T + (i - hist);
-                f.ra[r] = static_cast<const st*>(p.a)[tok * HV + c.hv];
-                f.rbw[r] = static_cast<const st*>(p.b)[tok * HV + c.hv];
-            }
+            const int ph = (c.base + (i < hl ? i : hl)) & (L - 1);
+            const int tw = i - hist < 0 ? 0 : (i - hist < T ? i - hist : T - 1);
+            const size_t idx = (static_cast<size_t>(c.b) * T + tw) * HV + c.hv;
+            const size_t w = Act::bytes == 2 ? idx >> 1 : idx;
+            f.rg[r] = p.rg[gbase + ph];
+            f.rb[r] = p.rb[gbase + ph];
+            f.ra[r] = static_cast<const uint32_t*>(p.a)[w];
+            f.rbw[r] = static_cast<const uint32_t*>(p.b)[w];
         }
     }
+}
+
+// Checkpoint loads of quarter Q (of K / 16 per lane): the item's 64 KB are
+// issued in four groups spread over its phases, so the memory pipe sees a
+// steady stream instead of one burst per item.
+template <int K, int Q>
+__device__ __forceinline__ void load_ckpt(f32x4 (&sraw)[K / 16], const float* Srow)
+{
+    constexpr int N = K / 64;
+#pragma unroll
+    for (int i = Q * N; i < (Q + 1) * N; ++i)
+        sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + 16 * i));
 }
 
 // Back substitution through block I of (I + A)^T m = f.  Lane j holds the
@@ -390,22 +450,32 @@ __device__ __forceinline__ void solve_block(const float* As, int lane, float& ac
     constexpr int RS = panel_stride(I);
     constexpr int W = 16 * (I + 1);
     const float* pr = As + panel_base(I) + lane;
+    // the block's 16 rows of A are read up front; the chain then runs from registers
     if constexpr (W <= 64) {
         if (lane < W) {
+            float a[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                a[r] = pr[r * RS];
 #pragma unroll
             for (int r = 15; r >= 0; --r) {
                 const float m = readlane_f(acc0, 16 * I + r);
-                acc0 = __builtin_fmaf(-pr[r * RS], m, acc0);
+                acc0 = __builtin_fmaf(-a[r], m, acc0);
             }
         }
     } else {
         const bool upd1 = lane + 64 < W;
+        float a0[16], a1[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            a0[r] = pr[r * RS];
+            a1[r] = pr[r * RS + 64];
+        }
 #pragma unroll
         for (int r = 15; r >= 0; --r) {
             const float m = readlane_f(acc1, 16 * I + r - 64);
-            acc0 = __builtin_fmaf(-pr[r * RS], m, acc0);
-            const float a1 = pr[r * RS + 64];
-            acc1 = upd1 ? __builtin_fmaf(-a1, m, acc1) : acc1;
+            acc0 = __builtin_fmaf(-a0[r], m, acc0);
+            acc1 = upd1 ? __builtin_fmaf(-a1[r], m, acc1) : acc1;
         }
     }
 }
@@ -508,11 +578,9 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         const int lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero)));
         const int tid = wave * 64 + lane;
         const int col = lane & 15, grp = lane >> 4;
-        // scalars of the next item (the last item repeats itself)
-        const Item nxt = next_item(p, cur);
         if (!cur.valid) {                      // padding row: nothing to read or write
-            issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
-            cur = nxt;
+            cur = next_item(p, cur);           // (the last item repeats itself)
+            issue_prefetch<Cfg, Act>(p, cur, tid, pf);
             continue;
         }
         const int s = cur.s, b = cur.b, hv = cur.hv, vt = cur.vt;
@@ -522,14 +590,13 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         const int NQ0 = NB << 4;        // first query row of X
         const int BV = p.BV;
 
-        // ============ 1. checkpoint rows of this wave (non-temporal stream)
+        // ============ 1. checkpoint rows of this wave (non-temporal stream,
+        // first quarter; the rest follow at the next phase boundaries)
         const bool has_rows = wave * 16 < BV;
         const int r0 = vt * BV + (has_rows ? wave * 16 : 0);
         const float* Srow = p.S + ((static_cast<size_t>(s) * p.HV + hv) * p.V + r0 + col) * K + 4 * grp;
         f32x4 sraw[K / 16];
-#pragma unroll
-        for (int i = 0; i < K / 16; ++i)
-            sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + 16 * i));
+        load_ckpt<K, 0>(sraw, Srow);
 
         // ============ 2. staging from the prefetch registers
         const bool write_ring = p.write_ring != 0;
@@ -547,7 +614,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             }
             ss = lane_group_sum<CPR>(ss);
             if (row < hist && ch == 0)
-                rn[row] = 1.0f / sqrtf(ss + p.eps);
+                rn[row] = rnorm_hw(ss, p.eps);
         }
         // window keys (rows hist..n-1) and queries (rows NQ0..NQ0+T-1)
 #pragma unroll
@@ -568,7 +635,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             }
             ss = lane_group_sum<CPR>(ss);
             if (live && ch == 0)
-                rn[row] = 1.0f / sqrtf(ss + p.eps);
+                rn[row] = rnorm_hw(ss, p.eps);
         }
         // key rows n..NQ0-1 are zero (they pad the last Gram block)
         for (int cc = tid; cc < (NQ0 - n) * CPR; cc += kThreads) {
@@ -616,8 +683,9 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                     gl[r] = pf.rg[r];
                     bl[r] = pf.rb[r];
                 } else if (i < n) {
-                    gdn_gate(act_f32<Act>(pf.ra[r]), act_f32<Act>(pf.rbw[r]), p.A_log[hv], p.dt_bias[hv],
-                             p.softplus_threshold, gl[r], bl[r]);
+                    const size_t idx = (static_cast<size_t>(b) * T + (i - hist)) * p.HV + hv;
+                    gdn_gate(act_from_word<Act>(pf.ra[r], idx), act_from_word<Act>(pf.rbw[r], idx), ld_uniform(p.A_log, hv),
+                             ld_uniform(p.dt_bias, hv), p.softplus_threshold, gl[r], bl[r]);
                     if (write_ring && vt == 0) {
                         const int ph = (base + wpc + (i - hist)) & (L - 1);
                         p.rg[gbase + ph] = gl[r];
@@ -626,16 +694,8 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 }
                 pair += gl[r];
             }
-            float incl = pair;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(incl, off, 64);
-                if (lane >= off)
-                    incl += y;
-            }
-            float run = __shfl_up(incl, 1, 64);
-            if (lane == 0)
-                run = 0.0f;
+            const float incl = wave_incl_scan(pair);
+            float run = dpp0<0x138, 0xF>(incl);   // wave_shr:1: the exclusive prefix
 #pragma unroll
             for (int r = 0; r < Cfg::RPL; ++r) {
                 const int i = Cfg::RPL * lane + r;
@@ -698,9 +758,13 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 *reinterpret_cast<f32x4*>(FU + t * FST + j4) = val;
             }
         }
-        // the next item's inputs stream in behind the rest of this one
-        issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
+        load_ckpt<K, 1>(sraw, Srow);
         __syncthreads();
+
+        // the next item's inputs stream in behind the rest of this one
+        const Item nxt = next_item(p, cur);
+        issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
+        load_ckpt<K, 2>(sraw, Srow);
 
         // ============ 4. M = (I + A)^{-T} F, one window column per wave
         for (int t = wave; t < TP; t += kWaves) {
@@ -722,6 +786,8 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         }
         __syncthreads();
 
+        load_ckpt<K, 3>(sraw, Srow);
+
         // ============ 5. Z = C^T X (keys) + the query terms, on MFMA 4x4x1:
         // unit (tg, kset): window columns 4 tg .. +3, key columns 64 kset + lane.
         constexpr int NKS = K / 64;
@@ -730,16 +796,26 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             const float* crow = Cs + (4 * tg + (lane & 3)) * CST;
             const int kc = 64 * ks + lane;
             f32x4 z0 = {0.0f, 0.0f, 0.0f, 0.0f}, z1 = z0;
+            // software pipelined: the next four rows are read before this
+            // step's products (reads past n stay inside X and C and are unused)
+            f32x4 c4 = *reinterpret_cast<const f32x4*>(crow);
+            float x0 = x_elem<kF32>(Xhi, Xlo, 0 * KP + kc), x1 = x_elem<kF32>(Xhi, Xlo, 1 * KP + kc);
+            float x2 = x_elem<kF32>(Xhi, Xlo, 2 * KP + kc), x3 = x_elem<kF32>(Xhi, Xlo, 3 * KP + kc);
             for (int i = 0; i < n; i += 4) {
-                const f32x4 c4 = *reinterpret_cast<const f32x4*>(crow + i);
-                const float x0 = x_elem<kF32>(Xhi, Xlo, (i + 0) * KP + kc);
-                const float x1 = x_elem<kF32>(Xhi, Xlo, (i + 1) * KP + kc);
-                const float x2 = x_elem<kF32>(Xhi, Xlo, (i + 2) * KP + kc);
-                const float x3 = x_elem<kF32>(Xhi, Xlo, (i + 3) * KP + kc);
+                const f32x4 cn = *reinterpret_cast<const f32x4*>(crow + i + 4);
+                const float y0 = x_elem<kF32>(Xhi, Xlo, (i + 4) * KP + kc);
+                const float y1 = x_elem<kF32>(Xhi, Xlo, (i + 5) * KP + kc);
+                const float y2 = x_elem<kF32>(Xhi, Xlo, (i + 6) * KP + kc);
+                const float y3 = x_elem<kF32>(Xhi, Xlo, (i + 7) * KP + kc);
                 z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[0], x0, z0, 0, 0, 0);
                 z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[1], x1, z1, 0, 0, 0);
                 z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[2], x2, z0, 0, 0, 0);
                 z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[3], x3, z1, 0, 0, 0);
+                c4 = cn;
+                x0 = y0;
+                x1 = y1;
+                x2 = y2;
+                x3 = y3;
             }
             // lane l, register r: Z[4 tg + r][kc]; add e^{Gam_{h+t}} rn_q q_t
 #pragma unroll
