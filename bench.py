@@ -48,6 +48,12 @@ def parse():
     ap.add_argument("--no-snapshot", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain device copy of COPY_BYTES "
+                         "(the reference for scaling the HBM byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="no GPU work: write the profile summary from the rocprofv3 CSVs "
+                         "under DIR/kt, DIR/fetch and DIR/write")
     return ap.parse_args()
 
 
@@ -109,6 +115,9 @@ def cpu_threads() -> int:
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the path shards by rows and value heads with no exchange; "
@@ -268,6 +277,14 @@ def main():
                    "checkpoint_bytes_per_layer": sh.num_slots * sh.HV * sh.V * sh.K * 4},
     }
 
+    if args.copy_calibration:
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
     if not args.no_snapshot:
         snap = torch.empty(sh.B, sh.T, sh.HV, sh.V, sh.K, dtype=torch.float32, device=dev)
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -298,6 +315,91 @@ def main():
         result["cpu_baseline"] = cpu_baseline(sh, args.seed, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 256 << 20
+PROFILE_CMDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/kt -o run --output-format csv -- "
+    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-snapshot --copy-calibration "
+    "> $R/gpurun_out/prof/kt.log 2>&1",
+    "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run --output-format csv -- "
+    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run --output-format csv -- "
+    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --copy-calibration",
+    "cd $R && python3 bench.py --summarize-profile gpurun_out/prof",
+]
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(d):
+    """Profile summary (markdown) from one kernel-trace run and two counter\n    runs of this script: the verify kernel's average duration over the timed\n    steps, and its HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by what the\n    same counters read for a plain copy of COPY_BYTES."""
+    steps_kt, steps_pmc = 20, 5
+    trace = [r for r in _csv(os.path.join(d, "kt", "run_kernel_trace.csv"))]
+    stats = _csv(os.path.join(d, "kt", "run_kernel_stats.csv"))
+    ver = [r for r in trace if "verify_kernel" in r["Kernel_Name"]]
+    timed = ver[-steps_kt:]
+    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed]) * 1e-3
+    vname = timed[-1]["Kernel_Name"]
+
+    def counter(sub, name):
+        rows = _csv(os.path.join(d, sub, "run_counter_collection.csv"))
+        rows = [r for r in rows if r["Counter_Name"] == name]
+        v = [float(r["Counter_Value"]) for r in rows if "verify_kernel" in r["Kernel_Name"]][-steps_pmc:]
+        c = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()][-3:]
+        return float(np.mean(v)), float(np.mean(c))
+
+    fv, fc = counter("fetch", "FETCH_SIZE")
+    wv, wc = counter("write", "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    f_fetch, f_write = kib / fc, kib / wc
+    hbm = (fv * f_fetch + wv * f_write) * 1024.0
+    alg = None
+    try:
+        for line in open(os.path.join(d, "kt.log")):
+            if line.startswith("{"):
+                alg = json.loads(line)["roofline"]["alg_bytes_per_launch"]
+    except OSError:
+        pass
+    src_hash = hashlib.sha256(open(VERIFY_SRC, "rb").read()).hexdigest()[:16]
+    out = []
+    out.append("# verify_kernel, GDN layer B=256 (qwen3next_b256 workload)\n")
+    out.append("Commands (from the repository root on the GPU host, `R=$PWD`; each profiler run under "
+               "its own `timeout`):\n")
+    out.append("```\n" + "\n".join(PROFILE_CMDS) + "\n```\n")
+    out.append(f"- kernel source: `linear_attention_speculative_spec_amd/csrc/gdn_verify.hip`, "
+               f"source sha256[:16]: `{src_hash}`")
+    out.append(f"- dispatch: `{vname}`")
+    out.append(f"- timed steps (last {steps_kt} verify dispatches of the kernel-trace run): "
+               f"average {dur.mean():.1f} us, min {dur.min():.1f} us, max {dur.max():.1f} us\n")
+    out.append("## --kernel-trace --stats (all dispatches of the run)\n")
+    out.append("| kernel | calls | average us | total ms | % |")
+    out.append("|---|---|---|---|---|")
+    for r in stats[:8]:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) * 1e-3:.1f} | "
+                   f"{float(r['TotalDurationNs']) * 1e-6:.2f} | {float(r['Percentage']):.1f} |")
+    out.append("\nThe verify's stats line also averages the ring pre-fill calls (one-token windows) and "
+               "the dry run; the timed-step average above is the figure bench.py's HIP events report.\n")
+    out.append("## HBM bytes (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)\n")
+    out.append("| | FETCH_SIZE KiB | WRITE_SIZE KiB |")
+    out.append("|---|---|---|")
+    out.append(f"| verify_kernel, mean of the last {steps_pmc} dispatches | {fv:.0f} | {wv:.0f} |")
+    out.append(f"| plain copy of {COPY_BYTES >> 20} MiB (mean of 3) | {fc:.0f} | {wc:.0f} |")
+    out.append(f"\nScale factors (copy bytes / counter): fetch {f_fetch:.4f}, write {f_write:.4f}.\n")
+    out.append(f"HBM bytes per launch (scaled): {hbm:.6e}")
+    if alg:
+        out.append(f"\nAlgorithmic bytes per launch (bench.py accounting): {alg:.6e} "
+                   f"(counter / algorithmic = {hbm / alg:.3f})")
+    path = PROFILE_SUMMARY
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def cpu_baseline(sh, seed, budget_s):

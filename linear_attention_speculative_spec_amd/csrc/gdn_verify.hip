@@ -30,9 +30,10 @@
 //      one wave forms the gates and their prefix sums;
 //   3. Gram tiles k k^T and k q^T on MFMA 16x16x32 bf16 (exact products of raw
 //      bf16 keys) scaled into the strictly lower A (stored as one dense panel
-//      per 16-row block) and F; the next item's inputs are issued;
-//   4. M by back substitution, one window column per wave: per row one LDS
-//      read, one lane broadcast and one FMA; then U and the coefficients of Z;
+//      per 16-row block) and F;
+//   4. the next item's inputs are issued; M by back substitution, one window
+//      column per wave: the block's A values are read up front, then per row
+//      one lane broadcast and one FMA; then U and the coefficients of Z;
 //   5. Z = C^T X on MFMA 4x4x1 (16 blocks: 64 key columns x 4 window columns
 //      per instruction, no padding at T = 4) while the other waves form the
 //      value part U^T V of their rows on the same instruction;
