@@ -35,8 +35,9 @@
 //      column per wave: the block's A values are read up front, then per row
 //      one lane broadcast and one FMA; then U and the coefficients of Z;
 //   5. Z = C^T X on MFMA 4x4x1 (16 blocks: 64 key columns x 4 window columns
-//      per instruction, no padding at T = 4) while the other waves form the
-//      value part U^T V of their rows on the same instruction;
+//      per instruction, no padding at T = 4; the query terms are four more
+//      coefficient rows) while the other waves form the value part U^T V of
+//      their rows on the same instruction;
 //   6. S0 Z for each wave's 16 rows on MFMA 4x4x1 straight from the checkpoint
 //      registers (4 key-column groups summed by lane-half swaps), plus the
 //      value part, scaled and stored.
@@ -90,14 +91,15 @@ struct VCfg {
     static constexpr int KP = K + 8;               // LDS X row, bf16 elements (16-byte pad)
     static constexpr int NXR = LM + 16;            // X rows: keys (< LM), 16 query rows at NQ0
     static constexpr int VP = BVM + EPC;           // LDS value row, activations (16-byte pad)
-    static constexpr int FST = LM + 4;             // F / U row stride (floats)
+    static constexpr int FST = LM + 20;            // F / U row stride (floats; U is zero past n)
     static constexpr int CST = LM + 20;            // Z coefficient row stride (floats)
     static constexpr int NBM = LM / 16;            // 16-row key blocks
     // A is stored per 16-row block I as a dense panel of 16 rows x 16 (I + 1)
     // columns (row stride 16 I + 20): only the part at or left of the block
     // diagonal exists.
     static constexpr int A_FLOATS = 128 * NBM * (NBM + 1) + 64 * NBM;
-    static constexpr int Z_FLOATS = 16 * K;
+    static constexpr int ZST = K + 4;             // Z row stride (floats; rows t on distinct banks)
+    static constexpr int Z_FLOATS = 16 * ZST;     // up to 16 window columns
     static constexpr int AZ = A_FLOATS > Z_FLOATS ? A_FLOATS : Z_FLOATS;
     static constexpr int VCRM = BVM / EPC;         // chunks per value row at most
     // register chunks per thread
@@ -110,7 +112,8 @@ struct VCfg {
     static constexpr size_t o_xhi = 0;
     static constexpr size_t o_xlo = o_xhi + static_cast<size_t>(NXR) * KP * 2;
     static constexpr size_t o_v = o_xlo + (kF32 ? static_cast<size_t>(NXR) * KP * 2 : 0);
-    static constexpr size_t o_az = o_v + align16c(static_cast<size_t>(LM) * VP * eb);
+    static constexpr int NVR = LM + 16;           // value rows: up to LM, then 16 zero rows
+    static constexpr size_t o_az = o_v + align16c(static_cast<size_t>(NVR) * VP * eb);
     static constexpr size_t o_fu = o_az + static_cast<size_t>(AZ) * 4;
     static constexpr size_t o_cs = o_fu + static_cast<size_t>(16) * FST * 4;
     static constexpr size_t o_rn = o_cs + static_cast<size_t>(16) * CST * 4;
@@ -274,6 +277,16 @@ __device__ __forceinline__ float x_elem(const uint16_t* Xhi, const uint16_t* Xlo
 
 // Activation element idx from the aligned 32-bit word that holds it (exact
 // widening).
+// LDS reads through 32-bit offsets in the LDS address space (generic
+// pointer arithmetic here is 64-bit, and its temporaries serialise reads).
+template <class T>
+__device__ __forceinline__ T lds_read(const void* base, uint32_t byte_off)
+{
+    typedef const __attribute__((address_space(3))) T* lptr;
+    typedef const __attribute__((address_space(3))) char* lbase;
+    return *((lptr)(((lbase)base) + byte_off));
+}
+
 template <class Act>
 __device__ __forceinline__ float act_from_word(uint32_t w, size_t idx)
 {
@@ -349,8 +362,6 @@ template <class Cfg, class Act>
 struct Prefetch {
     uint4 xh[Cfg::MH];
     uint4 xw[Cfg::MW];
-    uint4 vh[Cfg::MVH];
-    uint4 vw[Cfg::MVW];
     float rg[Cfg::RPL], rb[Cfg::RPL];
     uint32_t ra[Cfg::RPL], rbw[Cfg::RPL];   // aligned 32-bit words holding the activations
 };
@@ -373,38 +384,20 @@ __device__ __forceinline__ void issue_prefetch(const VerifyParams& p, const Item
     for (int m = 0; m < Cfg::MH; ++m) {
         const int cc = tid + kThreads * m;
         const int row = cc >> CSH, ch = cc & (CPR - 1);
+        f.xh[m] = uint4{0u, 0u, 0u, 0u};   // lanes without a row: no value flows in from elsewhere
         if (row < hist)
             f.xh[m] = ld16(ringk, static_cast<uint32_t>(((c.base + row) & (L - 1)) * (K * eb) + ch * 16));
     }
 #pragma unroll
     for (int m = 0; m < Cfg::MW; ++m) {
         const int cc = tid + kThreads * m;
+        f.xw[m] = uint4{0u, 0u, 0u, 0u};
         if (cc < 2 * T * CPR) {
             const bool isq = cc >= T * CPR;
             const int c2 = isq ? cc - T * CPR : cc;
             const uint32_t off = static_cast<uint32_t>((c2 >> CSH) * (H * K * eb) + (c2 & (CPR - 1)) * 16);
             f.xw[m] = ld16(isq ? qwin : kwin, off);
         }
-    }
-    // values: history from the ring (v head slab, this tile's columns), window v
-    const int VCR = 1 << p.vshift;
-    const size_t vrow = static_cast<size_t>(p.V) * eb;
-    const char* ringv = static_cast<const char*>(p.rawv) + (static_cast<size_t>(c.s) * HV + c.hv) * L * vrow +
-                        static_cast<size_t>(c.vt) * p.BV * eb;
-    const char* vwin = static_cast<const char*>(p.v) + (static_cast<size_t>(c.b) * T * HV + c.hv) * vrow +
-                       static_cast<size_t>(c.vt) * p.BV * eb;
-#pragma unroll
-    for (int m = 0; m < Cfg::MVH; ++m) {
-        const int cc = tid + kThreads * m;
-        const int row = cc >> p.vshift, ch = cc & (VCR - 1);
-        if (row < hist)
-            f.vh[m] = ld16(ringv, static_cast<uint32_t>(((c.base + row) & (L - 1)) * vrow + ch * 16));
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::MVW; ++m) {
-        const int cc = tid + kThreads * m;
-        if (cc < T * VCR)
-            f.vw[m] = ld16(vwin, static_cast<uint32_t>((cc >> p.vshift) * (HV * vrow) + (cc & (VCR - 1)) * 16));
     }
     // gate inputs of records RPL lane + r (the last wave forms the gates):
     // every lane loads all four, at clamped in-range indices, so no load is
@@ -438,6 +431,44 @@ __device__ __forceinline__ void load_ckpt(f32x4 (&sraw)[K / 16], const float* Sr
 #pragma unroll
     for (int i = Q * N; i < (Q + 1) * N; ++i)
         sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + 16 * i));
+}
+
+// The item's value rows (ring history and window, this tile's columns),
+// loaded at the start of the item and staged to LDS after the Gram tiles: a
+// short register live range, well ahead of their first use.
+template <class Cfg>
+struct ValueRows {
+    uint4 vh[Cfg::MVH];
+    uint4 vw[Cfg::MVW];
+};
+
+template <class Cfg>
+__device__ __forceinline__ void load_value_rows(const VerifyParams& p, const Item& c, int tid, ValueRows<Cfg>& f)
+{
+    constexpr int eb = Cfg::eb;
+    const int T = p.T, L = p.L, HV = p.HV;
+    const int hist = c.hist;
+    const int VCR = 1 << p.vshift;
+    const size_t vrow = static_cast<size_t>(p.V) * eb;
+    const char* ringv = static_cast<const char*>(p.rawv) + (static_cast<size_t>(c.s) * HV + c.hv) * L * vrow +
+                        static_cast<size_t>(c.vt) * p.BV * eb;
+    const char* vwin = static_cast<const char*>(p.v) + (static_cast<size_t>(c.b) * T * HV + c.hv) * vrow +
+                       static_cast<size_t>(c.vt) * p.BV * eb;
+#pragma unroll
+    for (int m = 0; m < Cfg::MVH; ++m) {
+        const int cc = tid + kThreads * m;
+        const int row = cc >> p.vshift, ch = cc & (VCR - 1);
+        f.vh[m] = uint4{0u, 0u, 0u, 0u};   // lanes without a row: no value flows in from elsewhere
+        if (row < hist)
+            f.vh[m] = ld16(ringv, static_cast<uint32_t>(((c.base + row) & (L - 1)) * vrow + ch * 16));
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::MVW; ++m) {
+        const int cc = tid + kThreads * m;
+        f.vw[m] = uint4{0u, 0u, 0u, 0u};
+        if (cc < T * VCR)
+            f.vw[m] = ld16(vwin, static_cast<uint32_t>((cc >> p.vshift) * (HV * vrow) + (cc & (VCR - 1)) * 16));
+    }
 }
 
 // Back substitution through block I of (I + A)^T m = f.  Lane j holds the
@@ -519,14 +550,23 @@ __device__ __forceinline__ f32x4 value_part(const float* FU, const typename Act:
     const int grp = lane >> 4;
     const float* urow = FU + (4 * tg + (lane & 3)) * Cfg::FST;
     f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
-    for (int m = 0; 4 * m < n; m += 2) {
-        const int i0 = 4 * m + grp, i1 = i0 + 4;
-        const bool ok0 = i0 < n, ok1 = i1 < n;
-        const float u0 = ok0 ? urow[i0] : 0.0f, u1 = ok1 ? urow[i1] : 0.0f;
-        const float v0 = ok0 ? Act::load(Vs + i0 * Cfg::VP + vcol) : 0.0f;
-        const float v1 = ok1 ? Act::load(Vs + i1 * Cfg::VP + vcol) : 0.0f;
-        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u0, v0, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u1, v1, a1, 0, 0, 0);
+    // sixteen rows per batch (i = 4 m + grp, m = m0..m0+3): reads first
+    for (int m0 = 0; 4 * m0 < n; m0 += 4) {
+        float u[4], v[4];
+        // U and the value rows are zero past n, so whole groups are read
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t i = static_cast<uint32_t>(4 * (m0 + e) + grp);
+            u[e] = lds_read<float>(urow, i * 4u);
+            if constexpr (Act::bytes == 2)
+                v[e] = bf16_to_f32(lds_read<uint16_t>(Vs, (i * Cfg::VP + vcol) * 2u));
+            else
+                v[e] = lds_read<float>(Vs, (i * Cfg::VP + vcol) * 4u);
+        }
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[0], v[0], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[1], v[1], a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[2], v[2], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[3], v[3], a1, 0, 0, 0);
     }
     return a0 + a1;
 }
@@ -565,10 +605,118 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
     cur.hv = (it / p.nvt) % p.HV;
     cur.b = it / p.nvt / p.HV;
     load_item_cursors(p, cur);
-    Prefetch<Cfg, Act> pf;
-    issue_prefetch<Cfg, Act>(p, cur, threadIdx.x, pf);
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    // Staging of item c from the prefetch registers into LDS: raw keys and
+    // queries (fp32 activations: bf16 hi + lo), their l2 norms reduced from
+    // the same registers, zero padding rows, the window's ring records
+    // (pre-mutation raw bits, single writer per qk head), and the gates with
+    // their prefix sums (last wave).  It runs while the previous item's
+    // outputs are formed: X, the norms and the gates are not read by that
+    // phase.
+    auto stage_keys = [&](const Item& c, const Prefetch<Cfg, Act>& pf, int tid, int lane, bool ring) {
+        const int s = c.s, b = c.b, hv = c.hv, vt = c.vt;
+        const int h = hv / G;
+        const int hist = c.hist, n = c.n, base = c.base, wpc = c.wpc;
+        const int NQ0 = ((n + 15) >> 4) << 4;
+            const bool write_ring = ring && p.write_ring != 0;
+            const bool k_writer = write_ring && (hv % G == 0) && vt == 0;
+            char* ringk = static_cast<char*>(p.rawk) + (static_cast<size_t>(s) * p.H + h) * L * K * Cfg::eb;
+            // history keys
+    #pragma unroll
+            for (int m = 0; m < Cfg::MH; ++m) {
+                const int cc = tid + kThreads * m;
+                const int row = cc >> CSH, ch = cc & (CPR - 1);
+                // the sum is formed on every lane (zero chunks on lanes
+                // without a row), so every load is consumed on every path
+                float ss = chunk_sumsq<Act>(pf.xh[m]);
+                if (row < hist)
+                    stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xh[m]);
+                ss = lane_group_sum<CPR>(ss);
+                if (row < hist && ch == 0)
+                    rn[row] = rnorm_hw(ss, p.eps);
+            }
+            // window keys (rows hist..n-1) and queries (rows NQ0..NQ0+T-1)
+    #pragma unroll
+            for (int m = 0; m < Cfg::MW; ++m) {
+                const int cc = tid + kThreads * m;
+                const bool live = cc < 2 * T * CPR;
+                const bool isq = cc >= T * CPR;
+                const int c2 = isq ? cc - T * CPR : cc;
+                const int t = c2 >> CSH, ch = c2 & (CPR - 1);
+                const int row = isq ? NQ0 + t : hist + t;
+                float ss = chunk_sumsq<Act>(pf.xw[m]);
+                if (live) {
+                    stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xw[m]);
+                    if (!isq && k_writer)
+                        st16(ringk, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * (K * Cfg::eb) + ch * 16),
+                             pf.xw[m]);
+                }
+                ss = lane_group_sum<CPR>(ss);
+                if (live && ch == 0)
+                    rn[row] = rnorm_hw(ss, p.eps);
+            }
+            // key rows n..NQ0-1 are zero (they pad the last Gram block), and so
+            // are query rows NQ0+T..NQ0+TP-1 (they pad the last group of Z rows)
+            const int nz = NQ0 - n;
+            for (int cc = tid; cc < (nz + TP - T) * CPR; cc += kThreads) {
+                const int zr = cc >> CSH, ch = cc & (CPR - 1);
+                const int row = zr < nz ? n + zr : NQ0 + T + (zr - nz);
+                const uint4 z = {0u, 0u, 0u, 0u};
+                stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, z);
+                if (ch == 0)
+                    rn[row] = 0.0f;
+            }
+            // gates of the combined sequence and their prefix sums (last wave)
+            if (wave == kWaves - 1) {
+                const size_t gbase = (static_cast<size_t>(s) * p.HV + hv) * L;
+                float gl[Cfg::RPL], bl[Cfg::RPL];
+                float pair = 0.0f;
+    #pragma unroll
+                for (int r = 0; r < Cfg::RPL; ++r) {
+                    const int i = Cfg::RPL * lane + r;
+                    gl[r] = 0.0f;
+                    bl[r] = 0.0f;
+                    if (i < hist) {
+                        gl[r] = pf.rg[r];
+                        bl[r] = pf.rb[r];
+                    } else if (i < n) {
+                        const size_t idx = (static_cast<size_t>(b) * T + (i - hist)) * p.HV + hv;
+                        gdn_gate(act_from_word<Act>(pf.ra[r], idx), act_from_word<Act>(pf.rbw[r], idx), ld_uniform(p.A_log, hv),
+                                 ld_uniform(p.dt_bias, hv), p.softplus_threshold, gl[r], bl[r]);
+                        if (write_ring && vt == 0) {
+                            const int ph = (base + wpc + (i - hist)) & (L - 1);
+                            p.rg[gbase + ph] = gl[r];
+                            p.rb[gbase + ph] = bl[r];
+                        }
+                    }
+                    pair += gl[r];
+                }
+                const float incl = wave_incl_scan(pair);
+                float run = dpp0<0x138, 0xF>(incl);   // wave_shr:1: the exclusive prefix
+    #pragma unroll
+                for (int r = 0; r < Cfg::RPL; ++r) {
+                    const int i = Cfg::RPL * lane + r;
+                    run += gl[r];
+                    gam[i] = run * kLog2e;
+                    bet[i] = bl[r];
+                }
+            }
+            // the gate registers count as consumed in every wave (only the
+            // last wave loaded them)
+#pragma unroll
+            for (int r = 0; r < Cfg::RPL; ++r)
+                asm volatile("" ::"v"(pf.rg[r]), "v"(pf.rb[r]), "v"(pf.ra[r]), "v"(pf.rbw[r]));
+    };
+
+    // the first item is staged here; every later one is staged before its
+    // turn (during the previous item's outputs, or right after a padding row)
+    {
+        const int tid0 = static_cast<int>(threadIdx.x);
+        Prefetch<Cfg, Act> pf0;
+        issue_prefetch<Cfg, Act>(p, cur, tid0, pf0);
+        stage_keys(cur, pf0, tid0, tid0 & 63, cur.valid != 0);
+    }
     for (; it < nitems; it += gridDim.x) {
         // The lane index is rebuilt in every iteration from an opaque zero
         // (mbcnt cannot be hoisted then): a thread id kept live across the
@@ -579,9 +727,16 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         const int lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero)));
         const int tid = wave * 64 + lane;
         const int col = lane & 15, grp = lane >> 4;
+        // the next item's raw keys, loaded while this one computes (declared
+        // per iteration: nothing flows through them from one item to the next)
+        Prefetch<Cfg, Act> pf;
         if (!cur.valid) {                      // padding row: nothing to read or write
             cur = next_item(p, cur);           // (the last item repeats itself)
+            // loads and staging are unconditional (a padding row or a repeated
+            // item stages harmlessly, with its ring writes off): a load on
+            // one path only would make later waits drain every load in flight
             issue_prefetch<Cfg, Act>(p, cur, tid, pf);
+            stage_keys(cur, pf, tid, lane, cur.valid && it + static_cast<int>(gridDim.x) < nitems);
             continue;
         }
         const int s = cur.s, b = cur.b, hv = cur.hv, vt = cur.vt;
@@ -598,113 +753,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         const float* Srow = p.S + ((static_cast<size_t>(s) * p.HV + hv) * p.V + r0 + col) * K + 4 * grp;
         f32x4 sraw[K / 16];
         load_ckpt<K, 0>(sraw, Srow);
+        ValueRows<Cfg> vr;
+        load_value_rows<Cfg>(p, cur, tid, vr);
 
-        // ============ 2. staging from the prefetch registers
-        const bool write_ring = p.write_ring != 0;
-        const bool k_writer = write_ring && (hv % G == 0) && vt == 0;
-        char* ringk = static_cast<char*>(p.rawk) + (static_cast<size_t>(s) * p.H + h) * L * K * Cfg::eb;
-        // history keys
-#pragma unroll
-        for (int m = 0; m < Cfg::MH; ++m) {
-            const int cc = tid + kThreads * m;
-            const int row = cc >> CSH, ch = cc & (CPR - 1);
-            float ss = 0.0f;
-            if (row < hist) {
-                stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xh[m]);
-                ss = chunk_sumsq<Act>(pf.xh[m]);
-            }
-            ss = lane_group_sum<CPR>(ss);
-            if (row < hist && ch == 0)
-                rn[row] = rnorm_hw(ss, p.eps);
-        }
-        // window keys (rows hist..n-1) and queries (rows NQ0..NQ0+T-1)
-#pragma unroll
-        for (int m = 0; m < Cfg::MW; ++m) {
-            const int cc = tid + kThreads * m;
-            const bool live = cc < 2 * T * CPR;
-            const bool isq = cc >= T * CPR;
-            const int c2 = isq ? cc - T * CPR : cc;
-            const int t = c2 >> CSH, ch = c2 & (CPR - 1);
-            const int row = isq ? NQ0 + t : hist + t;
-            float ss = 0.0f;
-            if (live) {
-                stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xw[m]);
-                ss = chunk_sumsq<Act>(pf.xw[m]);
-                if (!isq && k_writer)
-                    st16(ringk, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * (K * Cfg::eb) + ch * 16),
-                         pf.xw[m]);
-            }
-            ss = lane_group_sum<CPR>(ss);
-            if (live && ch == 0)
-                rn[row] = rnorm_hw(ss, p.eps);
-        }
-        // key rows n..NQ0-1 are zero (they pad the last Gram block)
-        for (int cc = tid; cc < (NQ0 - n) * CPR; cc += kThreads) {
-            const int row = n + (cc >> CSH), ch = cc & (CPR - 1);
-            const uint4 z = {0u, 0u, 0u, 0u};
-            stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, z);
-            if (ch == 0)
-                rn[row] = 0.0f;
-        }
-        // value rows of the tile
-        {
-            const int VCR = 1 << p.vshift;
-            const size_t vrow = static_cast<size_t>(p.V) * Cfg::eb;
-            char* ringv = static_cast<char*>(p.rawv) + (static_cast<size_t>(s) * p.HV + hv) * L * vrow +
-                          static_cast<size_t>(vt) * BV * Cfg::eb;
-#pragma unroll
-            for (int m = 0; m < Cfg::MVH; ++m) {
-                const int cc = tid + kThreads * m;
-                const int row = cc >> p.vshift, ch = cc & (VCR - 1);
-                if (row < hist)
-                    *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = pf.vh[m];
-            }
-#pragma unroll
-            for (int m = 0; m < Cfg::MVW; ++m) {
-                const int cc = tid + kThreads * m;
-                if (cc < T * VCR) {
-                    const int t = cc >> p.vshift, ch = cc & (VCR - 1);
-                    *reinterpret_cast<uint4*>(Vs + (hist + t) * VP + ch * EPC) = pf.vw[m];
-                    if (write_ring)
-                        st16(ringv, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * vrow + ch * 16), pf.vw[m]);
-                }
-            }
-        }
-        // gates of the combined sequence and their prefix sums (last wave)
-        if (wave == kWaves - 1) {
-            const size_t gbase = (static_cast<size_t>(s) * p.HV + hv) * L;
-            float gl[Cfg::RPL], bl[Cfg::RPL];
-            float pair = 0.0f;
-#pragma unroll
-            for (int r = 0; r < Cfg::RPL; ++r) {
-                const int i = Cfg::RPL * lane + r;
-                gl[r] = 0.0f;
-                bl[r] = 0.0f;
-                if (i < hist) {
-                    gl[r] = pf.rg[r];
-                    bl[r] = pf.rb[r];
-                } else if (i < n) {
-                    const size_t idx = (static_cast<size_t>(b) * T + (i - hist)) * p.HV + hv;
-                    gdn_gate(act_from_word<Act>(pf.ra[r], idx), act_from_word<Act>(pf.rbw[r], idx), ld_uniform(p.A_log, hv),
-                             ld_uniform(p.dt_bias, hv), p.softplus_threshold, gl[r], bl[r]);
-                    if (write_ring && vt == 0) {
-                        const int ph = (base + wpc + (i - hist)) & (L - 1);
-                        p.rg[gbase + ph] = gl[r];
-                        p.rb[gbase + ph] = bl[r];
-                    }
-                }
-                pair += gl[r];
-            }
-            const float incl = wave_incl_scan(pair);
-            float run = dpp0<0x138, 0xF>(incl);   // wave_shr:1: the exclusive prefix
-#pragma unroll
-            for (int r = 0; r < Cfg::RPL; ++r) {
-                const int i = Cfg::RPL * lane + r;
-                run += gl[r];
-                gam[i] = run * kLog2e;
-                bet[i] = bl[r];
-            }
-        }
+        // ============ 2. the keys were staged before this item's turn
+
         __syncthreads();
 
         // ============ 3. Gram tiles.  Block row I holds I + 1 tiles of A
@@ -759,6 +812,43 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 *reinterpret_cast<f32x4*>(FU + t * FST + j4) = val;
             }
         }
+        // value rows of the tile (loaded at the start of the item)
+        {
+            const bool write_ring = p.write_ring != 0;
+            const int VCR = 1 << p.vshift;
+            const size_t vrow = static_cast<size_t>(p.V) * Cfg::eb;
+            char* ringv = static_cast<char*>(p.rawv) + (static_cast<size_t>(s) * p.HV + hv) * L * vrow +
+                          static_cast<size_t>(vt) * BV * Cfg::eb;
+#pragma unroll
+            for (int m = 0; m < Cfg::MVH; ++m) {
+                const int cc = tid + kThreads * m;
+                const int row = cc >> p.vshift, ch = cc & (VCR - 1);
+                if (row < hist)
+                    *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = vr.vh[m];
+            }
+#pragma unroll
+            for (int m = 0; m < Cfg::MVW; ++m) {
+                const int cc = tid + kThreads * m;
+                if (cc < T * VCR) {
+                    const int t = cc >> p.vshift, ch = cc & (VCR - 1);
+                    *reinterpret_cast<uint4*>(Vs + (hist + t) * VP + ch * EPC) = vr.vw[m];
+                    if (write_ring)
+                        st16(ringv, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * vrow + ch * 16), vr.vw[m]);
+                }
+            }
+            // rows n..n+15 are zero: the value part reads whole 4-row groups
+            for (int cc = tid; cc < 16 * VCR; cc += kThreads) {
+                const int row = n + (cc >> p.vshift), ch = cc & (VCR - 1);
+                *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+        // the value-row registers count as consumed on every path
+#pragma unroll
+        for (int m = 0; m < Cfg::MVH; ++m)
+            asm volatile("" ::"v"(vr.vh[m].x), "v"(vr.vh[m].y), "v"(vr.vh[m].z), "v"(vr.vh[m].w));
+#pragma unroll
+        for (int m = 0; m < Cfg::MVW; ++m)
+            asm volatile("" ::"v"(vr.vw[m].x), "v"(vr.vw[m].y), "v"(vr.vw[m].z), "v"(vr.vw[m].w));
         load_ckpt<K, 1>(sraw, Srow);
         __syncthreads();
 
@@ -784,51 +874,56 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 FU[t * FST + j] = ok ? u : 0.0f;
                 Cs[t * CST + j] = ok ? cf : 0.0f;
             }
+            // U past the ring capacity is zero too (the value part reads
+            // whole 4-row groups); the query rows: e^{Gam_{h+t}} rn_q on the diagonal
+            if (lane < 16)
+                FU[t * FST + LM + lane] = 0.0f;
+            if (lane < 16)
+                Cs[t * CST + NQ0 + lane] =
+                    (lane == t && t < T) ? exp2_hw(gam[hist + t]) * rn[NQ0 + t] : 0.0f;
         }
         __syncthreads();
 
         load_ckpt<K, 3>(sraw, Srow);
 
-        // ============ 5. Z = C^T X (keys) + the query terms, on MFMA 4x4x1:
+        // ============ 5. Z = C^T X (keys, then the query rows) on MFMA 4x4x1:
         // unit (tg, kset): window columns 4 tg .. +3, key columns 64 kset + lane.
+        // Eight key rows per batch: every read is issued before the products.
         constexpr int NKS = K / 64;
+        constexpr int ZST = Cfg::ZST;
+        const int nk8 = (n + 7) & ~7;          // rows n..nk8-1 are zero rows (< NQ0)
         for (int u = wave; u < (TP / 4) * NKS; u += kWaves) {
             const int tg = u / NKS, ks = u % NKS;
             const float* crow = Cs + (4 * tg + (lane & 3)) * CST;
             const int kc = 64 * ks + lane;
             f32x4 z0 = {0.0f, 0.0f, 0.0f, 0.0f}, z1 = z0;
-            // software pipelined: the next four rows are read before this
-            // step's products (reads past n stay inside X and C and are unused)
-            f32x4 c4 = *reinterpret_cast<const f32x4*>(crow);
-            float x0 = x_elem<kF32>(Xhi, Xlo, 0 * KP + kc), x1 = x_elem<kF32>(Xhi, Xlo, 1 * KP + kc);
-            float x2 = x_elem<kF32>(Xhi, Xlo, 2 * KP + kc), x3 = x_elem<kF32>(Xhi, Xlo, 3 * KP + kc);
-            for (int i = 0; i < n; i += 4) {
-                const f32x4 cn = *reinterpret_cast<const f32x4*>(crow + i + 4);
-                const float y0 = x_elem<kF32>(Xhi, Xlo, (i + 4) * KP + kc);
-                const float y1 = x_elem<kF32>(Xhi, Xlo, (i + 5) * KP + kc);
-                const float y2 = x_elem<kF32>(Xhi, Xlo, (i + 6) * KP + kc);
-                const float y3 = x_elem<kF32>(Xhi, Xlo, (i + 7) * KP + kc);
-                z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[0], x0, z0, 0, 0, 0);
-                z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[1], x1, z1, 0, 0, 0);
-                z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[2], x2, z0, 0, 0, 0);
-                z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(c4[3], x3, z1, 0, 0, 0);
-                c4 = cn;
-                x0 = y0;
-                x1 = y1;
-                x2 = y2;
-                x3 = y3;
-            }
-            // lane l, register r: Z[4 tg + r][kc]; add e^{Gam_{h+t}} rn_q q_t
+            for (int i = 0; i < nk8; i += 8) {
+                const f32x4 ca = *reinterpret_cast<const f32x4*>(crow + i);
+                const f32x4 cb = *reinterpret_cast<const f32x4*>(crow + i + 4);
+                float x[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * tg + r;
-                float z = z0[r] + z1[r];
-                if (t < T) {
-                    const float cq = exp2_hw(gam[hist + t]) * rn[NQ0 + t];
-                    z = __builtin_fmaf(cq, x_elem<kF32>(Xhi, Xlo, (NQ0 + t) * KP + kc), z);
+                for (int e = 0; e < 8; ++e)
+                    x[e] = x_elem<kF32>(Xhi, Xlo, (i + e) * KP + kc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(ca[e], x[e], z0, 0, 0, 0);
+                    z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(cb[e], x[4 + e], z1, 0, 0, 0);
                 }
-                Zs[t * K + kc] = z;
             }
+            for (int i = NQ0; i < NQ0 + TP; i += 4) {
+                const f32x4 cq = *reinterpret_cast<const f32x4*>(crow + i);
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = x_elem<kF32>(Xhi, Xlo, (i + e) * KP + kc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    z0 = __builtin_amdgcn_mfma_f32_4x4x1f32(cq[e], x[e], z0, 0, 0, 0);
+            }
+            // lane l, register r: Z[4 tg + r][kc]
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Zs[(4 * tg + r) * ZST + kc] = z0[r] + z1[r];
         }
         // the value part of this wave's rows for the first four window columns
         const int vcol = wave * 16 + col;
@@ -836,6 +931,12 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         if (has_rows)
             vp0 = value_part<Cfg, Act>(FU, Vs, n, 0, lane, vcol);
         __syncthreads();
+
+        // the checkpoint registers count as consumed on every path (waves
+        // without rows load and drop them); no store is in flight yet
+#pragma unroll
+        for (int i = 0; i < K / 16; ++i)
+            asm volatile("" ::"v"(sraw[i][0]), "v"(sraw[i][1]), "v"(sraw[i][2]), "v"(sraw[i][3]));
 
         // ============ 6. O = S0 Z + V^T U for this wave's 16 rows.  Block
         // (kg = grp, rows 4 (col / 4) .. +3) sums key columns 16 i + 4 kg + e;
@@ -845,7 +946,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             for (int tg = 0; tg < TP / 4; ++tg) {
                 f32x4 a0 = tg == 0 ? vp0 : value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol);
                 f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f};
-                const float* zrow = Zs + (4 * tg + (lane & 3)) * K + 4 * grp;
+                const float* zrow = Zs + (4 * tg + (lane & 3)) * Cfg::ZST + 4 * grp;
 #pragma unroll
                 for (int i = 0; i < K / 16; ++i) {
                     const f32x4 za = *reinterpret_cast<const f32x4*>(zrow + 16 * i);
@@ -864,8 +965,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                         Act::from_f32(p.scale * val);
             }
         }
-        __syncthreads();   // LDS is restaged by the next item
-        cur = nxt;
+        // the next item's keys go to LDS after the outputs (its ring stores
+        // would otherwise sit in front of the checkpoint loads the outputs
+        // wait for)
+        stage_keys(nxt, pf, tid, lane, nxt.valid && it + static_cast<int>(gridDim.x) < nitems);
+        cur = nxt;   // the barrier after the next item's first loads orders the LDS reuse
     }
 }
 
