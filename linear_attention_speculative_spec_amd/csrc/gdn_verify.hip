@@ -63,6 +63,20 @@ struct VerifyParams {
     void* o;
 };
 
+// The launch arguments as seen in the kernel-argument segment (constant
+// address space).  The kernel reads them through a pointer it re-launders at
+// every phase boundary: each phase re-reads the fields it needs with scalar
+// loads, so no argument or product of arguments stays live across phases (kept
+// live, they overflow the scalar registers and every use becomes a VALU lane
+// read).
+typedef const __attribute__((address_space(4))) VerifyParams KParams;
+
+__device__ __forceinline__ KParams* launder(KParams* pk)
+{
+    asm volatile("" : "+s"(pk));
+    return pk;
+}
+
 // Fixed workgroup: 8 waves.  Waves whose 16 value rows fall outside the tile
 // only stage data and help with the key-side work.
 constexpr int kWaves = 8;
@@ -322,7 +336,7 @@ struct Item {
     int valid, s, b, hv, vt, hist, n, base, wpc;
 };
 
-__device__ __forceinline__ void load_item_cursors(const VerifyParams& p, Item& c)
+__device__ __forceinline__ void load_item_cursors(KParams& p, Item& c)
 {
     const int s = ld_uniform(p.slot_idx, c.b);
     c.valid = valid_slot(s, p.num_slots);
@@ -336,7 +350,7 @@ __device__ __forceinline__ void load_item_cursors(const VerifyParams& p, Item& c
 
 // The item after c in this workgroup's sequence: add the grid stride digit by
 // digit (no integer division per item).  Past the end the item is repeated.
-__device__ __forceinline__ Item next_item(const VerifyParams& p, const Item& c)
+__device__ __forceinline__ Item next_item(KParams& p, const Item& c)
 {
     Item d = c;
     int vt = c.vt + p.step_vt, hv = c.hv + p.step_hv, b = c.b + p.step_b;
@@ -367,7 +381,7 @@ struct Prefetch {
 };
 
 template <class Cfg, class Act>
-__device__ __forceinline__ void issue_prefetch(const VerifyParams& p, const Item& c, int tid,
+__device__ __forceinline__ void issue_prefetch(KParams& p, const Item& c, int tid,
                                                Prefetch<Cfg, Act>& f)
 {
     using st = typename Act::storage;
@@ -443,7 +457,7 @@ struct ValueRows {
 };
 
 template <class Cfg>
-__device__ __forceinline__ void load_value_rows(const VerifyParams& p, const Item& c, int tid, ValueRows<Cfg>& f)
+__device__ __forceinline__ void load_value_rows(KParams& p, const Item& c, int tid, ValueRows<Cfg>& f)
 {
     constexpr int eb = Cfg::eb;
     const int T = p.T, L = p.L, HV = p.HV;
@@ -572,7 +586,7 @@ __device__ __forceinline__ f32x4 value_part(const float* FU, const typename Act:
 }
 
 template <class Act, int K, int LM, int BVM, int MINW>
-__global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyParams p)
+__global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyParams p_arg)
 {
     using Cfg = VCfg<Act, K, LM, BVM>;
     using st = typename Act::storage;
@@ -593,18 +607,20 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
     float* gam = reinterpret_cast<float*>(smem + Cfg::o_gam); // log2(e) * prefix sums of g
     float* bet = reinterpret_cast<float*>(smem + Cfg::o_bet); // beta (0 past n)
 
-    const int nitems = p.B * p.HV * p.nvt;
-    const int T = p.T, L = p.L, G = p.HV / p.H;
+    (void)p_arg;   // read through the argument segment instead
+    KParams* pk = launder((KParams*)__builtin_amdgcn_kernarg_segment_ptr());
+    const int nitems = pk->B * pk->HV * pk->nvt;
+    const int T = pk->T, L = pk->L, G = pk->HV / pk->H;
     const int TP = (T + 3) & ~3;
 
     int it = blockIdx.x;
     if (it >= nitems)
         return;
     Item cur;
-    cur.vt = it % p.nvt;
-    cur.hv = (it / p.nvt) % p.HV;
-    cur.b = it / p.nvt / p.HV;
-    load_item_cursors(p, cur);
+    cur.vt = it % pk->nvt;
+    cur.hv = (it / pk->nvt) % pk->HV;
+    cur.b = it / pk->nvt / pk->HV;
+    load_item_cursors(*pk, cur);
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     // Staging of item c from the prefetch registers into LDS: raw keys and
@@ -615,13 +631,14 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
     // outputs are formed: X, the norms and the gates are not read by that
     // phase.
     auto stage_keys = [&](const Item& c, const Prefetch<Cfg, Act>& pf, int tid, int lane, bool ring) {
+        KParams* pk2 = launder(pk);
         const int s = c.s, b = c.b, hv = c.hv, vt = c.vt;
         const int h = hv / G;
         const int hist = c.hist, n = c.n, base = c.base, wpc = c.wpc;
         const int NQ0 = ((n + 15) >> 4) << 4;
-            const bool write_ring = ring && p.write_ring != 0;
+            const bool write_ring = ring && pk2->write_ring != 0;
             const bool k_writer = write_ring && (hv % G == 0) && vt == 0;
-            char* ringk = static_cast<char*>(p.rawk) + (static_cast<size_t>(s) * p.H + h) * L * K * Cfg::eb;
+            char* ringk = static_cast<char*>(pk2->rawk) + (static_cast<size_t>(s) * pk2->H + h) * L * K * Cfg::eb;
             // history keys
     #pragma unroll
             for (int m = 0; m < Cfg::MH; ++m) {
@@ -634,7 +651,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                     stage_x_chunk<Act>(Xhi + row * KP + ch * EPC, Xlo + row * KP + ch * EPC, pf.xh[m]);
                 ss = lane_group_sum<CPR>(ss);
                 if (row < hist && ch == 0)
-                    rn[row] = rnorm_hw(ss, p.eps);
+                    rn[row] = rnorm_hw(ss, pk2->eps);
             }
             // window keys (rows hist..n-1) and queries (rows NQ0..NQ0+T-1)
     #pragma unroll
@@ -654,7 +671,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 }
                 ss = lane_group_sum<CPR>(ss);
                 if (live && ch == 0)
-                    rn[row] = rnorm_hw(ss, p.eps);
+                    rn[row] = rnorm_hw(ss, pk2->eps);
             }
             // key rows n..NQ0-1 are zero (they pad the last Gram block), and so
             // are query rows NQ0+T..NQ0+TP-1 (they pad the last group of Z rows)
@@ -669,7 +686,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             }
             // gates of the combined sequence and their prefix sums (last wave)
             if (wave == kWaves - 1) {
-                const size_t gbase = (static_cast<size_t>(s) * p.HV + hv) * L;
+                const size_t gbase = (static_cast<size_t>(s) * pk2->HV + hv) * L;
                 float gl[Cfg::RPL], bl[Cfg::RPL];
                 float pair = 0.0f;
     #pragma unroll
@@ -681,13 +698,13 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                         gl[r] = pf.rg[r];
                         bl[r] = pf.rb[r];
                     } else if (i < n) {
-                        const size_t idx = (static_cast<size_t>(b) * T + (i - hist)) * p.HV + hv;
-                        gdn_gate(act_from_word<Act>(pf.ra[r], idx), act_from_word<Act>(pf.rbw[r], idx), ld_uniform(p.A_log, hv),
-                                 ld_uniform(p.dt_bias, hv), p.softplus_threshold, gl[r], bl[r]);
+                        const size_t idx = (static_cast<size_t>(b) * T + (i - hist)) * pk2->HV + hv;
+                        gdn_gate(act_from_word<Act>(pf.ra[r], idx), act_from_word<Act>(pf.rbw[r], idx), ld_uniform(pk2->A_log, hv),
+                                 ld_uniform(pk2->dt_bias, hv), pk2->softplus_threshold, gl[r], bl[r]);
                         if (write_ring && vt == 0) {
                             const int ph = (base + wpc + (i - hist)) & (L - 1);
-                            p.rg[gbase + ph] = gl[r];
-                            p.rb[gbase + ph] = bl[r];
+                            pk2->rg[gbase + ph] = gl[r];
+                            pk2->rb[gbase + ph] = bl[r];
                         }
                     }
                     pair += gl[r];
@@ -714,10 +731,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
     {
         const int tid0 = static_cast<int>(threadIdx.x);
         Prefetch<Cfg, Act> pf0;
-        issue_prefetch<Cfg, Act>(p, cur, tid0, pf0);
+        issue_prefetch<Cfg, Act>(*pk, cur, tid0, pf0);
         stage_keys(cur, pf0, tid0, tid0 & 63, cur.valid != 0);
     }
     for (; it < nitems; it += gridDim.x) {
+        pk = launder(pk);
         // The lane index is rebuilt in every iteration from an opaque zero
         // (mbcnt cannot be hoisted then): a thread id kept live across the
         // loop would be spilled, and its reload waits behind the in-flight
@@ -731,11 +749,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         // per iteration: nothing flows through them from one item to the next)
         Prefetch<Cfg, Act> pf;
         if (!cur.valid) {                      // padding row: nothing to read or write
-            cur = next_item(p, cur);           // (the last item repeats itself)
+            cur = next_item(*pk, cur);           // (the last item repeats itself)
             // loads and staging are unconditional (a padding row or a repeated
             // item stages harmlessly, with its ring writes off): a load on
             // one path only would make later waits drain every load in flight
-            issue_prefetch<Cfg, Act>(p, cur, tid, pf);
+            issue_prefetch<Cfg, Act>(*pk, cur, tid, pf);
             stage_keys(cur, pf, tid, lane, cur.valid && it + static_cast<int>(gridDim.x) < nitems);
             continue;
         }
@@ -744,21 +762,22 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         const int hist = cur.hist, n = cur.n, base = cur.base, wpc = cur.wpc;
         const int NB = (n + 15) >> 4;   // 16-row key blocks
         const int NQ0 = NB << 4;        // first query row of X
-        const int BV = p.BV;
+        const int BV = pk->BV;
 
         // ============ 1. checkpoint rows of this wave (non-temporal stream,
         // first quarter; the rest follow at the next phase boundaries)
         const bool has_rows = wave * 16 < BV;
         const int r0 = vt * BV + (has_rows ? wave * 16 : 0);
-        const float* Srow = p.S + ((static_cast<size_t>(s) * p.HV + hv) * p.V + r0 + col) * K + 4 * grp;
+        const float* Srow = pk->S + ((static_cast<size_t>(s) * pk->HV + hv) * pk->V + r0 + col) * K + 4 * grp;
         f32x4 sraw[K / 16];
         load_ckpt<K, 0>(sraw, Srow);
         ValueRows<Cfg> vr;
-        load_value_rows<Cfg>(p, cur, tid, vr);
+        load_value_rows<Cfg>(*pk, cur, tid, vr);
 
         // ============ 2. the keys were staged before this item's turn
 
         __syncthreads();
+        pk = launder(pk);
 
         // ============ 3. Gram tiles.  Block row I holds I + 1 tiles of A
         // (J <= I) and one tile of F (its keys against the queries).
@@ -772,17 +791,24 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             const int rowA = 16 * (ftile ? I : J) + col;   // MFMA rows m: keys j
             const int rowB = (ftile ? NQ0 : 16 * I) + col; // MFMA columns n: keys i or queries t
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            // all operand reads of the tile before the first product
+            bf16x8 xa[KS], xb[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = 32 * ks + 8 * grp;
-                const bf16x8 xa = *reinterpret_cast<const bf16x8*>(Xhi + rowA * KP + off);
-                const bf16x8 xb = *reinterpret_cast<const bf16x8*>(Xhi + rowB * KP + off);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, xb, acc, 0, 0, 0);
+                const uint32_t off = 32 * ks + 8 * grp;
+                xa[ks] = lds_read<bf16x8>(Xhi, (static_cast<uint32_t>(rowA) * KP + off) * 2u);
+                xb[ks] = lds_read<bf16x8>(Xhi, (static_cast<uint32_t>(rowB) * KP + off) * 2u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ks], xb[ks], acc, 0, 0, 0);
                 if constexpr (kF32) {
-                    const bf16x8 la = *reinterpret_cast<const bf16x8*>(Xlo + rowA * KP + off);
-                    const bf16x8 lb = *reinterpret_cast<const bf16x8*>(Xlo + rowB * KP + off);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, lb, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la, xb, acc, 0, 0, 0);
+                    const uint32_t off = 32 * ks + 8 * grp;
+                    const bf16x8 la = lds_read<bf16x8>(Xlo, (static_cast<uint32_t>(rowA) * KP + off) * 2u);
+                    const bf16x8 lb = lds_read<bf16x8>(Xlo, (static_cast<uint32_t>(rowB) * KP + off) * 2u);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ks], lb, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la, xb[ks], acc, 0, 0, 0);
                 }
             }
             // lane (col, grp) holds rows j = 16 (I or J) + 4 grp + jj of column col
@@ -814,15 +840,15 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         }
         // value rows of the tile (loaded at the start of the item)
         {
-            const bool write_ring = p.write_ring != 0;
-            const int VCR = 1 << p.vshift;
-            const size_t vrow = static_cast<size_t>(p.V) * Cfg::eb;
-            char* ringv = static_cast<char*>(p.rawv) + (static_cast<size_t>(s) * p.HV + hv) * L * vrow +
+            const bool write_ring = pk->write_ring != 0;
+            const int VCR = 1 << pk->vshift;
+            const size_t vrow = static_cast<size_t>(pk->V) * Cfg::eb;
+            char* ringv = static_cast<char*>(pk->rawv) + (static_cast<size_t>(s) * pk->HV + hv) * L * vrow +
                           static_cast<size_t>(vt) * BV * Cfg::eb;
 #pragma unroll
             for (int m = 0; m < Cfg::MVH; ++m) {
                 const int cc = tid + kThreads * m;
-                const int row = cc >> p.vshift, ch = cc & (VCR - 1);
+                const int row = cc >> pk->vshift, ch = cc & (VCR - 1);
                 if (row < hist)
                     *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = vr.vh[m];
             }
@@ -830,7 +856,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             for (int m = 0; m < Cfg::MVW; ++m) {
                 const int cc = tid + kThreads * m;
                 if (cc < T * VCR) {
-                    const int t = cc >> p.vshift, ch = cc & (VCR - 1);
+                    const int t = cc >> pk->vshift, ch = cc & (VCR - 1);
                     *reinterpret_cast<uint4*>(Vs + (hist + t) * VP + ch * EPC) = vr.vw[m];
                     if (write_ring)
                         st16(ringv, static_cast<uint32_t>(((base + wpc + t) & (L - 1)) * vrow + ch * 16), vr.vw[m]);
@@ -838,7 +864,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             }
             // rows n..n+15 are zero: the value part reads whole 4-row groups
             for (int cc = tid; cc < 16 * VCR; cc += kThreads) {
-                const int row = n + (cc >> p.vshift), ch = cc & (VCR - 1);
+                const int row = n + (cc >> pk->vshift), ch = cc & (VCR - 1);
                 *reinterpret_cast<uint4*>(Vs + row * VP + ch * EPC) = uint4{0u, 0u, 0u, 0u};
             }
         }
@@ -851,10 +877,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             asm volatile("" ::"v"(vr.vw[m].x), "v"(vr.vw[m].y), "v"(vr.vw[m].z), "v"(vr.vw[m].w));
         load_ckpt<K, 1>(sraw, Srow);
         __syncthreads();
+        pk = launder(pk);
 
         // the next item's inputs stream in behind the rest of this one
-        const Item nxt = next_item(p, cur);
-        issue_prefetch<Cfg, Act>(p, nxt, tid, pf);
+        const Item nxt = next_item(*pk, cur);
+        issue_prefetch<Cfg, Act>(*pk, nxt, tid, pf);
         load_ckpt<K, 2>(sraw, Srow);
 
         // ============ 4. M = (I + A)^{-T} F, one window column per wave
@@ -883,6 +910,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                     (lane == t && t < T) ? exp2_hw(gam[hist + t]) * rn[NQ0 + t] : 0.0f;
         }
         __syncthreads();
+        pk = launder(pk);
 
         load_ckpt<K, 3>(sraw, Srow);
 
@@ -910,7 +938,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                     z1 = __builtin_amdgcn_mfma_f32_4x4x1f32(cb[e], x[4 + e], z1, 0, 0, 0);
                 }
             }
-            for (int i = NQ0; i < NQ0 + TP; i += 4) {
+            for (int i = NQ0; i < NQ0 + TP; i += 4) {   // the query rows
                 const f32x4 cq = *reinterpret_cast<const f32x4*>(crow + i);
                 float x[4];
 #pragma unroll
@@ -931,6 +959,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         if (has_rows)
             vp0 = value_part<Cfg, Act>(FU, Vs, n, 0, lane, vcol);
         __syncthreads();
+        pk = launder(pk);
 
         // the checkpoint registers count as consumed on every path (waves
         // without rows load and drop them); no store is in flight yet
@@ -942,14 +971,20 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         // (kg = grp, rows 4 (col / 4) .. +3) sums key columns 16 i + 4 kg + e;
         // the four kg partial sums meet by lane swaps.
         if (has_rows) {
-            st* out = static_cast<st*>(p.o);
+            st* out = static_cast<st*>(pk->o);
             for (int tg = 0; tg < TP / 4; ++tg) {
                 f32x4 a0 = tg == 0 ? vp0 : value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol);
                 f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f};
                 const float* zrow = Zs + (4 * tg + (lane & 3)) * Cfg::ZST + 4 * grp;
+                // all of this lane's Z values are read before the first product
+                f32x4 zall[K / 16];
+#pragma unroll
+                for (int i = 0; i < K / 16; ++i)
+                    zall[i] = lds_read<f32x4>(zrow, 64u * i);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < K / 16; ++i) {
-                    const f32x4 za = *reinterpret_cast<const f32x4*>(zrow + 16 * i);
+                    const f32x4 za = zall[i];
                     a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
                     a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], a1, 0, 0, 0);
                     a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
@@ -961,10 +996,11 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 const float val = grp == 0 ? o0 : grp == 1 ? o1 : grp == 2 ? o2 : o3;
                 const int t = 4 * tg + grp;
                 if (t < T)
-                    out[((static_cast<size_t>(b) * T + t) * p.HV + hv) * p.V + r0 + col] =
-                        Act::from_f32(p.scale * val);
+                    out[((static_cast<size_t>(b) * T + t) * pk->HV + hv) * pk->V + r0 + col] =
+                        Act::from_f32(pk->scale * val);
             }
         }
+        pk = launder(pk);
         // the next item's keys go to LDS after the outputs (its ring stores
         // would otherwise sit in front of the checkpoint loads the outputs
         // wait for)
