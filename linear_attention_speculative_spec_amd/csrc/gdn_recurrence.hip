@@ -255,21 +255,41 @@ __global__ __launch_bounds__(256) void fold_kernel(const RecParams p, int num_la
 {
     __shared__ FoldShared<Act, K> sh;
     __shared__ int rows[kFoldRows];
+    __shared__ int wcount[4];
     __shared__ int nrows;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int tiles = p.V / 16;
     const int per_row = num_layers * p.HV * tiles;
     for (int c0 = 0; c0 < p.B; c0 += kFoldRows) {
+        const int cend = min(c0 + kFoldRows, p.B);
         if (tid == 0)
             nrows = 0;
         __syncthreads();
-        for (int r = c0 + tid; r < min(c0 + kFoldRows, p.B); r += 256) {
-            const int s = p.slot_idx[r];
-            if (valid_slot(s, p.num_slots) && (!p.only_flagged || p.is_flush[s] != 0) &&
-                clamp_wp(p.write_pos[s], p.L, p.T) > 0)
-                rows[atomicAdd(&nrows, 1)] = r;
+        // Compaction in row order (ballot + prefix counts): every workgroup
+        // must build the same list, since work items are indexed into it.
+        for (int r0 = c0; r0 < cend; r0 += 256) {
+            const int r = r0 + tid;
+            bool keep = false;
+            if (r < cend) {
+                const int s = p.slot_idx[r];
+                keep = valid_slot(s, p.num_slots) && (!p.only_flagged || p.is_flush[s] != 0) &&
+                       clamp_wp(p.write_pos[s], p.L, p.T) > 0;
+            }
+            const unsigned long long m = __ballot(keep);
+            if (lane == 0)
+                wcount[wave] = __popcll(m);
+            __syncthreads();
+            int pos = nrows + __popcll(m & ((1ull << lane) - 1ull));
+            for (int w = 0; w < wave; ++w)
+                pos += wcount[w];
+            if (keep)
+                rows[pos] = r;
+            __syncthreads();
+            if (tid == 0)
+                nrows += wcount[0] + wcount[1] + wcount[2] + wcount[3];
+            __syncthreads();
         }
-        __syncthreads();
         const int nitems = nrows * per_row;
         for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
             const int row = rows[it / per_row];

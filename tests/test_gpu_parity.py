@@ -277,10 +277,14 @@ def test_cache_base_shift_gives_identical_outputs():
 
 # ------------------------------------------------ snapshot baseline and fold
 
-def test_snapshot_matches_oracle_and_fold_reproduces_it_bitwise():
-    shape = synth.CONFIGS["qwen3next_b32"]
+@pytest.mark.parametrize("name", ["qwen3next_b32", "qwen3next_b256"])
+def test_snapshot_matches_oracle_and_fold_reproduces_it_bitwise(name):
+    # at B=256 every row is folded (rows spread over all waves of the fold's
+    # row compaction); the oracle follows a sample of rows
+    shape = synth.CONFIGS[name]
     wp0 = np.zeros(shape.num_slots, np.int32)            # empty history everywhere
-    P = Pair(shape, 2400, wp_by_slot=wp0)
+    orows = None if shape.B <= 32 else np.sort(synth.make_rng(2401).choice(shape.B, 8, replace=False))
+    P = Pair(shape, 2400, wp_by_slot=wp0, oracle_rows=orows)
     g = P.gpu
     win = P.window()
     dwin = DevWindow(win, shape.act)
@@ -301,7 +305,8 @@ def test_snapshot_matches_oracle_and_fold_reproduces_it_bitwise():
     # snapshot outputs and states against the oracle
     o_ref, snap_ref = P.orc.snapshot(P.oslots, helpers.win_f64(helpers.window_rows(win, P.orows, shape.T), shape.act))
     assert helpers.max_rel(P.gpu_out_rows(o_snap), o_ref) <= TOL[shape.act]
-    assert helpers.max_rel(host_f64(snap)[P.orows], snap_ref) <= TOL[shape.act]
+    sel = torch.from_numpy(np.asarray(P.orows, np.int64)).to("cuda:0")
+    assert helpers.max_rel(host_f64(snap.index_select(0, sel)), snap_ref) <= TOL[shape.act]
     assert helpers.max_rel(P.gpu_out_rows(o), o_ref) <= TOL[shape.act]
     # fold the recorded window by accept count: bit-identical to snap[b, a-1]
     acc = P.rng.integers(0, shape.T + 1, size=shape.B).astype(np.int32)
