@@ -213,3 +213,53 @@ def ring_garbage_template(rng, shape: LayerShape, num_layers: int = 1) -> dict:
         "g": nan_bits32(int(np.prod(lead + (S, HV, L)))).view(np.float32).reshape(lead + (S, HV, L)),
         "beta": nan_bits32(int(np.prod(lead + (S, HV, L)))).view(np.float32).reshape(lead + (S, HV, L)),
     }
+
+
+class DeviceWindows:
+    """Seeded draft windows drawn on the device, for long runs.
+
+    Same distributions as ``window`` (``beta_high`` moves b's mean to 4), drawn
+    by torch's seeded device generator in fp32 and rounded to the activation
+    dtype by torch's conversion (round to nearest even).  Host drawing would
+    dominate runs of thousands of verifies; the CPU side of a parity check
+    reads back the exact bits of the rows it follows (``host_rows``).
+    """
+
+    def __init__(self, seed: int, shape: LayerShape, variant: str = "base",
+                 device: str = "cuda:0"):
+        import torch
+
+        self.torch = torch
+        self.shape = shape
+        self.variant = variant
+        self.device = device
+        self.gen = torch.Generator(device=device)
+        self.gen.manual_seed(seed)
+        self.dtype = torch.bfloat16 if shape.act == ACT_BF16 else torch.float32
+
+    def normal(self, size, mean: float = 0.0):
+        t = self.torch.randn(size, generator=self.gen, device=self.device,
+                             dtype=self.torch.float32)
+        if mean:
+            t += mean
+        return t.to(self.dtype)
+
+    def draw(self, n_tok: int | None = None) -> dict:
+        sh = self.shape
+        n = sh.B * sh.T if n_tok is None else n_tok
+        bmean = 4.0 if self.variant == "beta_high" else 0.0
+        return {"q": self.normal((n, sh.H, sh.K)), "k": self.normal((n, sh.H, sh.K)),
+                "v": self.normal((n, sh.HV, sh.V)), "a": self.normal((n, sh.HV)),
+                "b": self.normal((n, sh.HV), bmean)}
+
+    def host_rows(self, win: dict, rows, T: int) -> Window:
+        """The given rows' tokens as a host ``Window`` (bf16 as uint16 bits)."""
+        torch = self.torch
+        idx = (np.asarray(rows)[:, None] * T + np.arange(T)[None, :]).reshape(-1)
+        sel = torch.from_numpy(idx.astype(np.int64)).to(self.device)
+        out = []
+        for name in ("q", "k", "v", "a", "b"):
+            x = win[name].index_select(0, sel).cpu()
+            out.append(x.view(torch.int16).numpy().view(np.uint16) if self.shape.act == ACT_BF16
+                       else x.numpy().astype(np.float32))
+        return Window(*out)

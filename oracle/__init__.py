@@ -98,10 +98,13 @@ def _ptr(x, kind=_dp):
 
 
 def default_threads() -> int:
+    """Host threads for the pair loop: the affinity mask, capped by OMP_NUM_THREADS."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = int(os.environ.get("OMP_NUM_THREADS", n) or n)
+    return max(1, min(n, cap))
 
 
 # ------------------------------------------------------------- scalar pieces
