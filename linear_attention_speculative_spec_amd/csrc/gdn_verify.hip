@@ -749,6 +749,10 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         // per iteration: nothing flows through them from one item to the next)
         Prefetch<Cfg, Act> pf;
         if (!cur.valid) {                      // padding row: nothing to read or write
+            // every wave is done staging the padding item before the next
+            // one is staged over it (rows are assigned to threads by position
+            // in the window, so two items' rows land on different waves)
+            __syncthreads();
             cur = next_item(*pk, cur);           // (the last item repeats itself)
             // loads and staging are unconditional (a padding row or a repeated
             // item stages harmlessly, with its ring writes off): a load on

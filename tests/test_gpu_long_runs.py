@@ -31,7 +31,8 @@ from linear_attention_speculative_spec_amd import gdnverify as gv
 from linear_attention_speculative_spec_amd import synth
 
 import helpers
-from gpu_harness import DEV, Pair, dev_cursors, dev_i32, host_cursors, host_f64, require_gpu
+from gpu_harness import (DEV, Pair, dev_cursors, dev_i32, host_bits, host_cursors, host_f64,
+                         require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +100,40 @@ def test_bandwidth_batch_b256_sampled_rows():
         advance(P.cur, P.slots, acc, shape.L, shape.T, shape.max_spec)
         advance(P.ocur, P.oslots, acc[P.orows], shape.L, shape.T, shape.max_spec)
         _cursors_equal(P.dcur, P.cur, step_i)
+
+
+def test_padding_rows_interleaved_at_full_size():
+    """B=256 with half the rows padding, alternating along every workgroup's
+    sequence of items (rows 16 apart): the valid rows' outputs are bitwise
+    those of the same call without padding, padding rows are left untouched,
+    and sampled valid rows match the oracle."""
+    require_gpu()
+    shape = synth.CONFIGS["qwen3next_b256"]
+    rng = synth.make_rng(1202)
+    pad = (np.arange(shape.B) // 16) % 2 == 1
+    pad |= rng.random(shape.B) < 0.1
+    valid_rows = np.flatnonzero(~pad)
+    pick = np.sort(rng.choice(valid_rows, 6, replace=False))
+    P = Pair(shape, 1202, oracle_rows=pick)
+    g = P.gpu
+    win = P.window()
+    dwin = helpers_devwin(win, shape.act)
+    o_full = g.new_out()
+    g.verify(P.dcur, P.dslots, dwin, o_full, write_ring=0, fold_flagged=0)
+    slots = P.slots.copy()
+    slots[pad] = -1
+    slots[np.flatnonzero(pad)[::7]] = shape.num_slots       # out of range counts as padding too
+    o_pad = g.new_out()
+    sentinel = host_bits(o_pad)
+    g.verify(P.dcur, dev_i32(slots), dwin, o_pad, write_ring=0, fold_flagged=0)
+    a, b_ = host_bits(o_full), host_bits(o_pad)
+    tok_valid = np.repeat(~pad, shape.T)
+    assert np.array_equal(b_[tok_valid], a[tok_valid]), "valid rows changed by padding elsewhere"
+    assert np.array_equal(b_[~tok_valid], sentinel[~tok_valid]), "padding rows written"
+    ref = P.oracle_verify(win, write_ring=False, fold_flagged=False)
+    err = helpers.max_rel(P.gpu_out_rows(o_pad), ref)
+    say(f"padding interleaved: {int(pad.sum())} padding rows, max_rel(o) = {err:.2e}")
+    assert err <= TOL[shape.act]
 
 
 def helpers_devwin(win: synth.Window, act: str):
