@@ -41,8 +41,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # long enough for the clocks to settle (the first few milliseconds of
+    # work run measurably slower)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-snapshot", action="store_true")
@@ -321,7 +323,7 @@ COPY_BYTES = 256 << 20
 PROFILE_CMDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/kt -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-snapshot --copy-calibration "
+    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --copy-calibration "
     "> $R/gpurun_out/prof/kt.log 2>&1",
     "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --copy-calibration",
@@ -339,7 +341,7 @@ def _csv(path):
 
 def summarize_profile(d):
     """Profile summary (markdown) from one kernel-trace run and two counter\n    runs of this script: the verify kernel's average duration over the timed\n    steps, and its HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by what the\n    same counters read for a plain copy of COPY_BYTES."""
-    steps_kt, steps_pmc = 20, 5
+    steps_kt, steps_pmc = 50, 5
     trace = [r for r in _csv(os.path.join(d, "kt", "run_kernel_trace.csv"))]
     stats = _csv(os.path.join(d, "kt", "run_kernel_stats.csv"))
     ver = [r for r in trace if "verify_kernel" in r["Kernel_Name"]]
