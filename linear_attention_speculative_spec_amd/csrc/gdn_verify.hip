@@ -888,6 +888,10 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         issue_prefetch<Cfg, Act>(*pk, nxt, tid, pf);
         load_ckpt<K, 2>(sraw, Srow);
 
+        // the waves on the critical path of the solve and of Z issue first
+        // (the other workgroup on the unit runs its own phases meanwhile)
+        if (wave < TP)
+            __builtin_amdgcn_s_setprio(2);
         // ============ 4. M = (I + A)^{-T} F, one window column per wave
         for (int t = wave; t < TP; t += kWaves) {
             float acc0 = FU[t * FST + lane];
@@ -916,6 +920,10 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         __syncthreads();
         pk = launder(pk);
 
+        if (wave < (TP / 4) * (K / 64))
+            __builtin_amdgcn_s_setprio(2);
+        else
+            __builtin_amdgcn_s_setprio(0);
         load_ckpt<K, 3>(sraw, Srow);
 
         // ============ 5. Z = C^T X (keys, then the query rows) on MFMA 4x4x1:
@@ -957,6 +965,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
             for (int r = 0; r < 4; ++r)
                 Zs[(4 * tg + r) * ZST + kc] = z0[r] + z1[r];
         }
+        __builtin_amdgcn_s_setprio(0);
         // the value part of this wave's rows for the first four window columns
         const int vcol = wave * 16 + col;
         f32x4 vp0 = {0.0f, 0.0f, 0.0f, 0.0f};
