@@ -974,19 +974,15 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         __syncthreads();
         pk = launder(pk);
 
-        // the checkpoint registers count as consumed on every path (waves
-        // without rows load and drop them); no store is in flight yet
-#pragma unroll
-        for (int i = 0; i < K / 16; ++i)
-            asm volatile("" ::"v"(sraw[i][0]), "v"(sraw[i][1]), "v"(sraw[i][2]), "v"(sraw[i][3]));
 
         // ============ 6. O = S0 Z + V^T U for this wave's 16 rows.  Block
         // (kg = grp, rows 4 (col / 4) .. +3) sums key columns 16 i + 4 kg + e;
         // the four kg partial sums meet by lane swaps.
         if (has_rows) {
             st* out = static_cast<st*>(pk->o);
-            for (int tg = 0; tg < TP / 4; ++tg) {
-                f32x4 a0 = tg == 0 ? vp0 : value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol);
+            // window columns 4 tg .. +3 (the first group is peeled off the loop,
+            // so its products can start as each checkpoint group lands)
+            auto out_group = [&](int tg, f32x4 a0) {
                 f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f};
                 const float* zrow = Zs + (4 * tg + (lane & 3)) * Cfg::ZST + 4 * grp;
                 // all of this lane's Z values are read before the first product
@@ -1011,7 +1007,15 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 if (t < T)
                     out[((static_cast<size_t>(b) * T + t) * pk->HV + hv) * pk->V + r0 + col] =
                         Act::from_f32(pk->scale * val);
-            }
+            };
+            out_group(0, vp0);
+            for (int tg = 1; tg < TP / 4; ++tg)
+                out_group(tg, value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol));
+        } else {
+            // waves without rows load the checkpoint registers too and drop them
+#pragma unroll
+            for (int i = 0; i < K / 16; ++i)
+                asm volatile("" ::"v"(sraw[i][0]), "v"(sraw[i][1]), "v"(sraw[i][2]), "v"(sraw[i][3]));
         }
         pk = launder(pk);
         // the next item's keys go to LDS after the outputs (its ring stores
