@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-snapshot", action="store_true")
+    ap.add_argument("--no-fold-every-commit", action="store_true",
+                    help="skip the comparison with the fold-every-commit design")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -313,6 +315,54 @@ def main():
             "draft_tokens_per_s": tokens / ((snap_us + commit_us) * 1e-6)}
         del snap
 
+    if not args.no_fold_every_commit:
+        # The other design the method admits: the ring holds only the window
+        # (2T records), every commit is folded into the checkpoint at once and
+        # the cursors are reset, so the verify never replays a history.  Same
+        # checkpoint, windows and accept counts; its own ring.
+        gsf = gs.replace(L=2 * sh.max_spec)
+        rkf = torch.zeros(sh.num_slots, sh.H, gsf.L, sh.K, dtype=torch.bfloat16, device=dev)
+        rvf = torch.zeros(sh.num_slots, sh.HV, gsf.L, sh.V, dtype=torch.bfloat16, device=dev)
+        rgf = torch.zeros(sh.num_slots, sh.HV, gsf.L, dtype=torch.float32, device=dev)
+        rbf = torch.zeros_like(rgf)
+        Sf = saved[0].clone()
+        curf = [i32(np.zeros(sh.num_slots)) for _ in range(3)]
+
+        def step_f(i, ev=None):
+            w = wins[i % n_pool]
+            if ev is not None:
+                ev[0].record()
+            gv.gdn_spec_verify_ring(gsf, *w, A_log, dt_bias, Sf, dslots, *curf, rkf, rvf, rgf, rbf,
+                                    1, 0, o)
+            if ev is not None:
+                ev[1].record()
+            gv.gdn_advance_cursors(gsf, dslots, acc_d[i % n_steps], *curf)
+            gv.gdn_exact_fold(gsf, 1, Sf, rkf, rvf, rgf, rbf, dslots, *curf, 0)
+            if ev is not None:
+                ev[2].record()
+            gv.gdn_reset_cursors(gsf, dslots, sh.B, 0, *curf)
+
+        for i in range(args.warmup):
+            step_f(i)
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for j in range(args.steps):
+            step_f(args.warmup + j, evf[j])
+        e1.record()
+        torch.cuda.synchronize()
+        f_step = e0.elapsed_time(e1) / args.steps * 1e3
+        result["fold_every_commit"] = {
+            "ring_len": gsf.L,
+            "step_us": f_step,
+            "verify_us": float(np.mean([e[0].elapsed_time(e[1]) for e in evf]) * 1e3),
+            "fold_us": float(np.mean([e[1].elapsed_time(e[2]) for e in evf]) * 1e3),
+            "draft_tokens_per_s": tokens / (f_step * 1e-6),
+            "ring_bytes_per_layer": gv.gdn_ring_bytes(gsf)}
+        log(f"[bench] fold every commit: step {f_step:.1f} us")
+        del rkf, rvf, rgf, rbf, Sf
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, args.seed, args.cpu_seconds)
 
@@ -323,12 +373,15 @@ COPY_BYTES = 256 << 20
 PROFILE_CMDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/kt -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --copy-calibration "
+    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "--copy-calibration "
     "> $R/gpurun_out/prof/kt.log 2>&1",
     "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --copy-calibration",
+    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "--copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --copy-calibration",
+    "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "--copy-calibration",
     "cd $R && python3 bench.py --summarize-profile gpurun_out/prof",
 ]
 

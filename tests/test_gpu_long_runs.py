@@ -141,6 +141,64 @@ def helpers_devwin(win: synth.Window, act: str):
     return DevWindow(win, act)
 
 
+# ------------------------------------------------- fold-every-commit design
+
+def test_fold_every_commit_matches_ring_with_history():
+    """The fold-every-commit design (a ring of 2T records holding only the
+    window; every commit folded into the checkpoint at once, then the cursors
+    reset) against the oracle, and against the ring-with-history design on the
+    same inputs and accept counts: both compute the same outputs, and the
+    committed states agree."""
+    require_gpu()
+    shape_r = synth.CONFIGS["qwen3next_b32"]
+    shape_f = shape_r.replace(L=2 * shape_r.max_spec)
+    steps = 12
+    zeros = np.zeros(shape_r.num_slots, np.int32)
+    Pr = Pair(shape_r, 2600, "low_decay", wp_by_slot=zeros, base_by_slot=zeros)
+    Pf = Pair(shape_f, 2600, "low_decay", wp_by_slot=zeros, base_by_slot=zeros, slots=Pr.slots)
+    assert np.array_equal(Pr.params.S0, Pf.params.S0)
+    wrng = synth.make_rng(2601)
+    accepts = synth.accept_counts(wrng, shape_r.B, shape_r.T, steps)
+    tol = TOL[shape_r.act]
+    for i in range(steps):
+        win = synth.window(wrng, shape_r, "low_decay")
+        dwin = helpers_devwin(win, shape_r.act)
+        acc = accepts[i]
+        # ring with history
+        o_r = Pr.gpu.new_out()
+        Pr.gpu.verify(Pr.dcur, Pr.dslots, dwin, o_r)
+        gv.gdn_advance_cursors(Pr.gpu.gs, Pr.dslots, dev_i32(acc), *Pr.dcur)
+        advance(Pr.cur, Pr.slots, acc, shape_r.L, shape_r.T, shape_r.max_spec)
+        _cursors_equal(Pr.dcur, Pr.cur, i)
+        # fold every commit: the verify sees no history
+        o_f = Pf.gpu.new_out()
+        Pf.gpu.verify(Pf.dcur, Pf.dslots, dwin, o_f, fold_flagged=0)
+        ref = Pf.oracle_verify(win, fold_flagged=False)
+        gv.gdn_advance_cursors(Pf.gpu.gs, Pf.dslots, dev_i32(acc), *Pf.dcur)
+        gv.gdn_exact_fold(Pf.gpu.gs, 1, Pf.gpu.S, *Pf.gpu.ring(), Pf.dslots, *Pf.dcur, 0)
+        gv.gdn_reset_cursors(Pf.gpu.gs, Pf.dslots, shape_f.B, 0, *Pf.dcur)
+        advance(Pf.ocur, Pf.oslots, acc, shape_f.L, shape_f.T, shape_f.max_spec)
+        Pf.orc.fold(Pf.ocur, Pf.oslots, only_flagged=False)
+        oracle.reset(Pf.ocur, Pf.oslots)
+        advance(Pf.cur, Pf.slots, acc, shape_f.L, shape_f.T, shape_f.max_spec)
+        oracle.reset(Pf.cur, Pf.slots)
+        _cursors_equal(Pf.dcur, Pf.cur, i)
+        err_o = helpers.max_rel(Pf.gpu_out_rows(o_f), ref)
+        err_rf = helpers.max_rel(host_f64(o_f), host_f64(o_r))
+        assert err_o <= tol, (i, err_o)
+        assert err_rf <= tol, (i, err_rf)
+    # the committed states: the history design folds what its ring still holds
+    S_r = Pr.gpu.S.clone()
+    fl = dev_i32(np.ones(shape_r.num_slots))
+    gv.gdn_exact_fold(Pr.gpu.gs, 1, S_r, *Pr.gpu.ring(), Pr.dslots, Pr.dcur[0], Pr.dcur[1], fl, 0)
+    sel = torch.from_numpy(Pr.slots.astype(np.int64)).to(DEV)
+    err_s = helpers.max_rel(host_f64(S_r.index_select(0, sel)), host_f64(Pf.gpu.S.index_select(0, sel)))
+    err_so = helpers.max_rel(host_f64(Pf.gpu.S.index_select(0, sel)), Pf.orc.S)
+    say(f"fold every commit: {steps} steps, checkpoints vs history design {err_s:.2e}, "
+        f"vs oracle {err_so:.2e}")
+    assert err_s <= tol and err_so <= tol
+
+
 # ------------------------------------------------- long-window drift, T=8 L=128
 
 def drift_run(variant: str, iters: int, seed: int, n_orows: int = 4, check_every: int = 32):
