@@ -382,8 +382,15 @@ PROFILE_CMDS = [
     "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
     "--copy-calibration",
+    "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_INSTS_VALU_MFMA_BF16 SQ_INSTS_VALU_MFMA_F32 GRBM_GUI_ACTIVE -d $R/gpurun_out/prof/mfma -o run "
+    "--output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot "
+    "--no-fold-every-commit",
     "cd $R && python3 bench.py --summarize-profile gpurun_out/prof",
 ]
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA peaks of the part
+SIMDS = 256 * 4
+XCDS = 8    # GRBM_GUI_ACTIVE is reported summed over the accelerator dies
 
 
 def _csv(path):
@@ -450,6 +457,36 @@ def summarize_profile(d):
     if alg:
         out.append(f"\nAlgorithmic bytes per launch (bench.py accounting): {alg:.6e} "
                    f"(counter / algorithmic = {hbm / alg:.3f})")
+    mdir = os.path.join(d, "mfma", "run_counter_collection.csv")
+    if os.path.exists(mdir):
+        rows = _csv(mdir)
+
+        def mc(name):
+            v = [float(r["Counter_Value"]) for r in rows
+                 if r["Counter_Name"] == name and "verify_kernel" in r["Kernel_Name"]][-steps_pmc:]
+            return float(np.mean(v))
+        mops_bf16, mops_f32 = mc("SQ_INSTS_VALU_MFMA_MOPS_BF16"), mc("SQ_INSTS_VALU_MFMA_MOPS_F32")
+        busy, gui = mc("SQ_VALU_MFMA_BUSY_CYCLES"), mc("GRBM_GUI_ACTIVE")
+        n_bf16, n_f32 = mc("SQ_INSTS_VALU_MFMA_BF16"), mc("SQ_INSTS_VALU_MFMA_F32")
+        fl_bf16, fl_f32 = mops_bf16 * 512, mops_f32 * 512
+        t = dur.mean() * 1e-6
+        out.append("\n## MFMA use (--pmc SQ_INSTS_VALU_MFMA_MOPS_*, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)\n")
+        out.append("The window algebra (Gram tiles in bf16; Z, the value part and S0 Z in fp32) is small "
+                   "beside the checkpoint stream; these counters show how much of the matrix units it "
+                   "occupies.\n")
+        out.append("| | bf16 | fp32 |")
+        out.append("|---|---|---|")
+        out.append(f"| MFMA instructions per launch | {n_bf16:.0f} | {n_f32:.0f} |")
+        out.append(f"| MFMA flops per launch (MOPS x 512) | {fl_bf16:.4e} | {fl_f32:.4e} |")
+        out.append(f"| achieved at the timed average ({dur.mean():.1f} us), TFLOP/s | "
+                   f"{fl_bf16 / t / 1e12:.2f} | {fl_f32 / t / 1e12:.2f} |")
+        out.append(f"| fraction of the dense peak ({MFMA_PEAK_TFLOPS['bf16']:.0f} / "
+                   f"{MFMA_PEAK_TFLOPS['f32']:.1f} TFLOP/s) | {fl_bf16 / t / 1e12 / MFMA_PEAK_TFLOPS['bf16']:.4f} | "
+                   f"{fl_f32 / t / 1e12 / MFMA_PEAK_TFLOPS['f32']:.4f} |")
+        out.append(f"\nSQ_VALU_MFMA_BUSY_CYCLES {busy:.4e}, GRBM_GUI_ACTIVE {gui:.4e} per launch "
+                   f"(summed over {XCDS} dies: {gui / XCDS:.4e} cycles each): matrix units busy "
+                   f"{100.0 * busy / (gui / XCDS * SIMDS):.2f}% of SIMD-cycles "
+                   f"(busy / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs)).")
     path = PROFILE_SUMMARY
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
