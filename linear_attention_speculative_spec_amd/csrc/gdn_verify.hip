@@ -191,6 +191,15 @@ __device__ __forceinline__ float rows4_sum(float x)
     return swap32_sum(swap16_sum(x));
 }
 
+// Sum over the eight lanes l + 8 c (c = 0..7) of a wave, delivered to every
+// one of them: l ^ 8 inside each 16-lane row by a DPP rotate, then the row
+// pairs and the halves by lane swaps.
+__device__ __forceinline__ float rows8_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    return rows4_sum(x);
+}
+
 // DPP move of x with row mask RM; lanes without a source (or outside the
 // mask) receive 0.
 template <int CTRL, int RM>
@@ -437,14 +446,18 @@ __device__ __forceinline__ void issue_prefetch(KParams& p, const Item& c, int ti
 
 // Checkpoint loads of quarter Q (of K / 16 per lane): the item's 64 KB are
 // issued in four groups spread over its phases, so the memory pipe sees a
-// steady stream instead of one burst per item.
+// steady stream instead of one burst per item.  Load i of lane l reads row
+// 8 (i & 1) + l % 8 of the wave's 16, key columns 32 (i >> 1) + 4 (l / 8) ..
+// +3: every load instruction covers whole 128-byte lines (8 rows x 128 B),
+// which streams measurably faster than 16 rows x 64 B.  Sl points at the
+// lane's first element (row l % 8, column 4 (l / 8)).
 template <int K, int Q>
-__device__ __forceinline__ void load_ckpt(f32x4 (&sraw)[K / 16], const float* Srow)
+__device__ __forceinline__ void load_ckpt(f32x4 (&sraw)[K / 16], const float* Sl)
 {
     constexpr int N = K / 64;
 #pragma unroll
     for (int i = Q * N; i < (Q + 1) * N; ++i)
-        sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + 16 * i));
+        sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sl + (i & 1) * 8 * K + (i >> 1) * 32));
 }
 
 // The item's value rows (ring history and window, this tile's columns),
@@ -554,35 +567,41 @@ __device__ __forceinline__ void solve_all(const float* As, int NB, int lane, flo
     }
 }
 
-// The value part of the outputs for window columns 4 tg .. 4 tg + 3 on MFMA
-// 4x4x1: block (kg = lane / 16, row group) takes ring/window rows i = 4 m + kg;
-// lane l gets its 16 value rows' sums over kg's rows only.
+// V^T U for this wave's 16 value rows and window columns 4 tg .. +3, in the
+// layout of the output products: MFMA 4x4x1 block b = l / 4 of lane l holds
+// value rows vrow0 + 8 h + 4 (b & 1) + (0..3) (h = 0: vp0, h = 1: vp1) and
+// sums the records i = 8 m + l / 8; the eight groups l / 8 meet with the
+// checkpoint products.  U and the value rows are zero past n, so whole
+// groups of eight records are read.
 template <class Cfg, class Act>
-__device__ __forceinline__ f32x4 value_part(const float* FU, const typename Act::storage* Vs, int n, int tg,
-                                            int lane, int vcol)
+__device__ __forceinline__ void value_part(const float* FU, const typename Act::storage* Vs, int n, int tg,
+                                           int lane, int vrow0, f32x4& vp0, f32x4& vp1)
 {
-    const int grp = lane >> 4;
+    const int c = lane >> 3;
     const float* urow = FU + (4 * tg + (lane & 3)) * Cfg::FST;
+    const int vc = vrow0 + (lane & 7);
     f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
-    // sixteen rows per batch (i = 4 m + grp, m = m0..m0+3): reads first
-    for (int m0 = 0; 4 * m0 < n; m0 += 4) {
-        float u[4], v[4];
-        // U and the value rows are zero past n, so whole groups are read
+    for (int m0 = 0; 8 * m0 < n; m0 += 2) {
+        float u[2], v0[2], v1[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t i = static_cast<uint32_t>(4 * (m0 + e) + grp);
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t i = static_cast<uint32_t>(8 * (m0 + e) + c);
             u[e] = lds_read<float>(urow, i * 4u);
-            if constexpr (Act::bytes == 2)
-                v[e] = bf16_to_f32(lds_read<uint16_t>(Vs, (i * Cfg::VP + vcol) * 2u));
-            else
-                v[e] = lds_read<float>(Vs, (i * Cfg::VP + vcol) * 4u);
+            if constexpr (Act::bytes == 2) {
+                v0[e] = bf16_to_f32(lds_read<uint16_t>(Vs, (i * Cfg::VP + vc) * 2u));
+                v1[e] = bf16_to_f32(lds_read<uint16_t>(Vs, (i * Cfg::VP + vc + 8) * 2u));
+            } else {
+                v0[e] = lds_read<float>(Vs, (i * Cfg::VP + vc) * 4u);
+                v1[e] = lds_read<float>(Vs, (i * Cfg::VP + vc + 8) * 4u);
+            }
         }
-        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[0], v[0], a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[1], v[1], a1, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[2], v[2], a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[3], v[3], a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[0], v0[0], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[0], v1[0], a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[1], v0[1], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(u[1], v1[1], a1, 0, 0, 0);
     }
-    return a0 + a1;
+    vp0 = a0;
+    vp1 = a1;
 }
 
 template <class Act, int K, int LM, int BVM, int MINW>
@@ -772,7 +791,8 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         // first quarter; the rest follow at the next phase boundaries)
         const bool has_rows = wave * 16 < BV;
         const int r0 = vt * BV + (has_rows ? wave * 16 : 0);
-        const float* Srow = pk->S + ((static_cast<size_t>(s) * pk->HV + hv) * pk->V + r0 + col) * K + 4 * grp;
+        const float* Srow = pk->S + ((static_cast<size_t>(s) * pk->HV + hv) * pk->V + r0 + (lane & 7)) * K +
+                            4 * (lane >> 3);
         f32x4 sraw[K / 16];
         load_ckpt<K, 0>(sraw, Srow);
         ValueRows<Cfg> vr;
@@ -967,50 +987,67 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         }
         __builtin_amdgcn_s_setprio(0);
         // the value part of this wave's rows for the first four window columns
-        const int vcol = wave * 16 + col;
-        f32x4 vp0 = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 vp0 = {0.0f, 0.0f, 0.0f, 0.0f}, vp1 = vp0;
         if (has_rows)
-            vp0 = value_part<Cfg, Act>(FU, Vs, n, 0, lane, vcol);
+            value_part<Cfg, Act>(FU, Vs, n, 0, lane, wave * 16, vp0, vp1);
         __syncthreads();
         pk = launder(pk);
 
 
         // ============ 6. O = S0 Z + V^T U for this wave's 16 rows.  Block
-        // (kg = grp, rows 4 (col / 4) .. +3) sums key columns 16 i + 4 kg + e;
-        // the four kg partial sums meet by lane swaps.
+        // b = l / 4 of lane l sums key columns 32 q + 4 (l / 8) + e for rows
+        // 8 h + 4 (b & 1) + (0..3) (h = 0 from the even loads, 1 from the odd
+        // ones); the eight key groups l / 8 meet by a rotate and lane swaps.
         if (has_rows) {
             st* out = static_cast<st*>(pk->o);
             // window columns 4 tg .. +3 (the first group is peeled off the loop,
             // so its products can start as each checkpoint group lands)
-            auto out_group = [&](int tg, f32x4 a0) {
-                f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f};
-                const float* zrow = Zs + (4 * tg + (lane & 3)) * Cfg::ZST + 4 * grp;
+            auto out_group = [&](int tg, f32x4 a0, f32x4 a1) {
+                f32x4 b0 = {0.0f, 0.0f, 0.0f, 0.0f}, b1 = b0;
+                const float* zrow = Zs + (4 * tg + (lane & 3)) * Cfg::ZST + 4 * (lane >> 3);
                 // all of this lane's Z values are read before the first product
-                f32x4 zall[K / 16];
+                f32x4 zall[K / 32];
 #pragma unroll
-                for (int i = 0; i < K / 16; ++i)
-                    zall[i] = lds_read<f32x4>(zrow, 64u * i);
+                for (int q = 0; q < K / 32; ++q)
+                    zall[q] = lds_read<f32x4>(zrow, 128u * q);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < K / 16; ++i) {
-                    const f32x4 za = zall[i];
-                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
-                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], a1, 0, 0, 0);
-                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
-                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], a1, 0, 0, 0);
+                    const f32x4 za = zall[i >> 1];
+                    if (i & 1) {
+                        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a1, 0, 0, 0);
+                        b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b1, 0, 0, 0);
+                        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a1, 0, 0, 0);
+                        b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b1, 0, 0, 0);
+                    } else {
+                        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
+                        b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b0, 0, 0, 0);
+                        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
+                        b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b0, 0, 0, 0);
+                    }
                 }
-                const f32x4 tot = a0 + a1;
-                const float o0 = rows4_sum(tot[0]), o1 = rows4_sum(tot[1]);
-                const float o2 = rows4_sum(tot[2]), o3 = rows4_sum(tot[3]);
-                const float val = grp == 0 ? o0 : grp == 1 ? o1 : grp == 2 ? o2 : o3;
-                const int t = 4 * tg + grp;
+                // lane l, register r: window column r of row 8 h + l % 8 (partial
+                // over key group l / 8); after the sums lane l stores half
+                // (l / 8) / 4, window column (l / 8) % 4
+                const f32x4 lo = a0 + b0, hi = a1 + b1;
+                const int c = lane >> 3;
+                float val = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sl = rows8_sum(lo[r]), sh = rows8_sum(hi[r]);
+                    val = c == r ? sl : (c == 4 + r ? sh : val);
+                }
+                const int t = 4 * tg + (c & 3);
                 if (t < T)
-                    out[((static_cast<size_t>(b) * T + t) * pk->HV + hv) * pk->V + r0 + col] =
+                    out[((static_cast<size_t>(b) * T + t) * pk->HV + hv) * pk->V + r0 + (lane & 7) + 8 * (c >> 2)] =
                         Act::from_f32(pk->scale * val);
             };
-            out_group(0, vp0);
-            for (int tg = 1; tg < TP / 4; ++tg)
-                out_group(tg, value_part<Cfg, Act>(FU, Vs, n, tg, lane, vcol));
+            out_group(0, vp0, vp1);
+            for (int tg = 1; tg < TP / 4; ++tg) {
+                f32x4 v0, v1;
+                value_part<Cfg, Act>(FU, Vs, n, tg, lane, wave * 16, v0, v1);
+                out_group(tg, v0, v1);
+            }
         } else {
             // waves without rows load the checkpoint registers too and drop them
 #pragma unroll
