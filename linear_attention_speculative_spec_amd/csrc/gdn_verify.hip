@@ -445,8 +445,9 @@ __device__ __forceinline__ void issue_prefetch(KParams& p, const Item& c, int ti
 }
 
 // Checkpoint loads of quarter Q (of K / 16 per lane): the item's 64 KB are
-// issued in four groups spread over its phases, so the memory pipe sees a
-// steady stream instead of one burst per item.  Load i of lane l reads row
+// issued in four groups (at the item's start, the Gram tiles, the solve and
+// the Z phase), so the memory pipe sees a steady stream instead of one burst
+// per item.  Load i of lane l reads row
 // 8 (i & 1) + l % 8 of the wave's 16, key columns 32 (i >> 1) + 4 (l / 8) ..
 // +3: every load instruction covers whole 128-byte lines (8 rows x 128 B),
 // which streams measurably faster than 16 rows x 64 B.  Sl points at the
@@ -806,6 +807,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         // ============ 3. Gram tiles.  Block row I holds I + 1 tiles of A
         // (J <= I) and one tile of F (its keys against the queries).
         const int ntiles = NB * (NB + 3) / 2;
+        load_ckpt<K, 1>(sraw, Srow);   // (after the value rows: their wait below leaves it in flight)
         for (int ti = wave; ti < ntiles; ti += kWaves) {
             int I = 0;
             while ((I + 1) * (I + 4) / 2 <= ti)
@@ -899,14 +901,14 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
 #pragma unroll
         for (int m = 0; m < Cfg::MVW; ++m)
             asm volatile("" ::"v"(vr.vw[m].x), "v"(vr.vw[m].y), "v"(vr.vw[m].z), "v"(vr.vw[m].w));
-        load_ckpt<K, 1>(sraw, Srow);
         __syncthreads();
         pk = launder(pk);
 
-        // the next item's inputs stream in behind the rest of this one
+        // the checkpoint's third quarter, then the next item's inputs, stream
+        // in behind the rest of this one
+        load_ckpt<K, 2>(sraw, Srow);
         const Item nxt = next_item(*pk, cur);
         issue_prefetch<Cfg, Act>(*pk, nxt, tid, pf);
-        load_ckpt<K, 2>(sraw, Srow);
 
         // the waves on the critical path of the solve and of Z issue first
         // (the other workgroup on the unit runs its own phases meanwhile)
