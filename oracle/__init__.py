@@ -58,7 +58,8 @@ class _Args(ctypes.Structure):
                 ("A_log", _dp), ("dt_bias", _dp),
                 ("o", _dp), ("snap", _dp),
                 ("fold_flagged", ctypes.c_int), ("only_flagged", ctypes.c_int),
-                ("pair_row", _ip), ("pair_hv", _ip), ("n_pairs", ctypes.c_int)]
+                ("pair_row", _ip), ("pair_hv", _ip), ("n_pairs", ctypes.c_int),
+                ("dwin", _dp), ("rd", _dp)]
 
 
 def _load():
@@ -77,6 +78,9 @@ def _load():
         lib.orc_step.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, _dp,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double]
         lib.orc_step.restype = None
+        lib.orc_step_d.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, _dp,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_double, _dp]
+        lib.orc_step_d.restype = None
         lib.orc_gate.argtypes = [ctypes.c_double] * 5 + [_dp, _dp]
         lib.orc_gate.restype = None
         lib.orc_rnorm.argtypes = [_dp, ctypes.c_int, ctypes.c_double]
@@ -130,6 +134,16 @@ def step(S, k_raw, v, g: float, beta: float, eps: float = 1e-6) -> np.ndarray:
     return S
 
 
+def step_d(S, k_raw, v, g: float, beta: float, eps: float = 1e-6):
+    """One step on a copy of S; returns (new S, corrected delta d [V])."""
+    S = _f64(S).copy()
+    k_raw, v = _f64(k_raw), _f64(v)
+    V, K = S.shape
+    d = np.empty(V)
+    _load().orc_step_d(_ptr(S), V, K, _ptr(k_raw), _ptr(v), g, beta, eps, _ptr(d))
+    return S, d
+
+
 def readout(S, q_raw, scale: float = 1.0, eps: float = 1e-6) -> np.ndarray:
     S, q_raw = _f64(S), _f64(q_raw)
     V, K = S.shape
@@ -157,6 +171,10 @@ class OracleLayer:
         self.rawv = np.full((sh.num_slots, sh.HV, sh.L, sh.V), np.nan)
         self.g = np.full((sh.num_slots, sh.HV, sh.L), np.nan)
         self.beta = np.full((sh.num_slots, sh.HV, sh.L), np.nan)
+        # ring of corrected deltas [num_slots, HV, L, V], made on first use
+        # by a d-cache verify
+        self.d = None
+        self.last_dwin = None
 
     def _args(self, cur, slot_idx, win=None, o=None, snap=None, pairs=None, shape=None):
         sh = shape or self.shape
@@ -188,10 +206,13 @@ class OracleLayer:
         return A, keep
 
     def verify(self, cur, slot_idx, win, write_ring=True, fold_flagged=True,
-               nthreads=None, pairs=None, T=None):
+               nthreads=None, pairs=None, T=None, dcache=False):
         """Outputs [B*T, HV, V] for every window position.
 
         ``win`` = (q, k, v, a, b) widened to float64, packed token-major.
+        With ``dcache`` the window's corrected deltas are kept in
+        ``last_dwin`` [B*T, HV, V] and, with ``write_ring``, recorded in the
+        d ring ``self.d`` beside the raw records.
         """
         sh = self.shape if T is None else self.shape.replace(T=T)
         B = len(slot_idx)
@@ -199,6 +220,11 @@ class OracleLayer:
         o = np.full((B * sh.T, sh.HV, sh.V), np.nan)
         A, keep = self._args(cur, slot_idx, win, o=o, pairs=pairs, shape=sh)
         A.fold_flagged = int(fold_flagged)
+        if dcache:
+            if self.d is None:
+                self.d = np.full((sh.num_slots, sh.HV, sh.L, sh.V), np.nan)
+            self.last_dwin = np.full((B * sh.T, sh.HV, sh.V), np.nan)
+            A.dwin, A.rd = _ptr(self.last_dwin), _ptr(self.d)
         _load().orc_verify(ctypes.byref(A), int(write_ring), nthreads or default_threads())
         del keep
         return o

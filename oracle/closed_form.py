@@ -75,3 +75,58 @@ def unit_lower_inverse(A: np.ndarray) -> np.ndarray:
         term = -term @ A
         out = out + term
     return out
+
+
+def deltas(S0, keys, values, g, beta, eps=1e-6):
+    """Corrected deltas D [n, V] of the combined sequence, from (I + A) D = R
+    solved by ``numpy.linalg.solve`` (the same system as ``window_outputs``)."""
+    S0 = np.asarray(S0, dtype=np.float64)
+    kh = normalise(keys, eps)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    n = kh.shape[0]
+    Gam = np.cumsum(g)
+    lower = np.tril(np.ones((n, n), dtype=bool), k=-1)
+    diff = Gam[:, None] - Gam[None, :]
+    decay = np.where(lower, np.exp(np.where(lower, diff, 0.0)), 0.0)
+    A = beta[:, None] * decay * (kh @ kh.T)
+    R = beta[:, None] * (values - np.exp(Gam)[:, None] * (kh @ S0.T))
+    return np.linalg.solve(np.eye(n) + A, R)
+
+
+def dcache_window(S0, d_hist, keys, values, g, beta, queries, hist, scale=1.0, eps=1e-6):
+    """The d-cache route to the same outputs (the first-generation d ring of
+    replayssm(B)SpecDecode §1.1): the committed history enters only through its
+    stored corrected deltas ``d_hist`` [hist, V]; the window's deltas follow
+    from a T x T unit lower-triangular system whose right-hand side has the
+    history's coupling removed,
+
+        (I + A_ww) D_w = R_w - A_wh D_h,
+
+    and the outputs are the closed form's, with D = [D_h; D_w].  Returns
+    (outputs [T, V], window deltas [T, V])."""
+    S0 = np.asarray(S0, dtype=np.float64)
+    kh = normalise(keys, eps)
+    qh = normalise(queries, eps)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    d_hist = np.asarray(d_hist, dtype=np.float64).reshape(hist, S0.shape[0])
+    n = kh.shape[0]
+    T = n - hist
+    Gam = np.cumsum(g)
+    w = np.arange(hist, n)
+    # window rows against every earlier record: A_ij for j < i
+    coup = beta[w, None] * np.exp(Gam[w, None] - Gam[None, :]) * (kh[w] @ kh.T)
+    coup = np.where(np.arange(n)[None, :] < w[:, None], coup, 0.0)
+    R = beta[w, None] * (values[w] - np.exp(Gam[w])[:, None] * (kh[w] @ S0.T))
+    rhs = R - coup[:, :hist] @ d_hist
+    D_w = np.linalg.solve(np.eye(T) + coup[:, hist:], rhs)
+    D = np.concatenate([d_hist, D_w], axis=0)
+    out = np.empty((T, S0.shape[0]))
+    for t in range(T):
+        i = hist + t
+        wt = np.exp(Gam[i] - Gam[: i + 1]) * (kh[: i + 1] @ qh[t])
+        out[t] = scale * (np.exp(Gam[i]) * (S0 @ qh[t]) + wt @ D[: i + 1])
+    return out, D_w

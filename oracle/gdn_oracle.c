@@ -58,6 +58,8 @@ typedef struct {
  *   q, k   [B*T][H][K]; v [B*T][HV][V]; a, b [B*T][HV]   window, token = row*T+t
  *   o      [B*T][HV][V]
  *   snap   [B][T][HV][V][K]
+ *   dwin   [B*T][HV][V]                   window corrected deltas (optional)
+ *   rd     [num_slots][HV][L][V]          ring: corrected deltas (optional)
  */
 typedef struct {
     orc_shape sh;
@@ -71,6 +73,8 @@ typedef struct {
     int only_flagged;     /* fold: skip rows whose slot is not flagged  */
     const int32_t *pair_row, *pair_hv;   /* optional (row, hv) subset   */
     int n_pairs;
+    double *dwin;         /* verify: corrected delta of each window step */
+    double *rd;           /* ring write: corrected deltas (needs dwin)    */
 } orc_args;
 
 /* ---------------------------------------------------------------- helpers */
@@ -95,9 +99,13 @@ double orc_rnorm(const double *x, int n, double eps)
     return 1.0 / sqrt(ss + eps);
 }
 
-/* One gated delta-rule step on a V x K state, with the raw key normalised. */
-void orc_step(double *S, int V, int K, const double *k_raw, const double *v,
-              double g, double beta, double eps)
+/* One gated delta-rule step on a V x K state, with the raw key normalised.
+ * d_out (optional, length V) receives the corrected delta of each state row,
+ * d = beta (v - e^g S k_hat): the rank-1 factor the step adds along k_hat
+ * (replayssm(B)SpecDecode §1.1 table and §12.6, the d ring of the first
+ * generation). */
+void orc_step_d(double *S, int V, int K, const double *k_raw, const double *v,
+                double g, double beta, double eps, double *d_out)
 {
     double rn = orc_rnorm(k_raw, K, eps);
     double decay = exp(g);
@@ -109,9 +117,17 @@ void orc_step(double *S, int V, int K, const double *k_raw, const double *v,
         for (int c = 0; c < K; c++)
             u += row[c] * (k_raw[c] * rn);
         double d = beta * (v[r] - u);
+        if (d_out)
+            d_out[r] = d;
         for (int c = 0; c < K; c++)
             row[c] += d * (k_raw[c] * rn);
     }
+}
+
+void orc_step(double *S, int V, int K, const double *k_raw, const double *v,
+              double g, double beta, double eps)
+{
+    orc_step_d(S, V, K, k_raw, v, g, beta, eps, NULL);
 }
 
 /* o[r] = scale * sum_c S[r][c] * q_hat[c] */
@@ -186,7 +202,8 @@ static void verify_pair(const orc_args *A, int row, int hv, double *Sw)
         const double *kt = A->k + (tok * sh->H + h) * sh->K;
         const double *vt = A->v + (tok * sh->HV + hv) * sh->V;
         const double *qt = A->q + (tok * sh->H + h) * sh->K;
-        orc_step(Sw, sh->V, sh->K, kt, vt, g, beta, sh->eps);
+        orc_step_d(Sw, sh->V, sh->K, kt, vt, g, beta, sh->eps,
+                   A->dwin ? A->dwin + (tok * sh->HV + hv) * sh->V : NULL);
         orc_readout(Sw, sh->V, sh->K, qt, sh->scale, sh->eps,
                     A->o + (tok * sh->HV + hv) * sh->V);
     }
@@ -303,6 +320,9 @@ static void write_window_records(const orc_args *A)
                 size_t gi = ((size_t)s * sh->HV + hv) * sh->L + p;
                 A->rg[gi] = g;
                 A->rb[gi] = beta;
+                if (A->rd && A->dwin)
+                    memcpy(A->rd + gi * sh->V, A->dwin + (tok * sh->HV + hv) * sh->V,
+                           sh->V * sizeof(double));
             }
         }
     }
@@ -311,7 +331,9 @@ static void write_window_records(const orc_args *A)
 /* ----------------------------------------------------------- entry points */
 
 /* Verify: outputs for every window position; folds flagged rows first when
- * fold_flagged; then (write_ring) records the window in the ring.  The ring
+ * fold_flagged; then (write_ring) records the window in the ring.  With dwin
+ * set it also returns each window step's corrected delta, and with rd set the
+ * ring write records those deltas beside the raw records (the d-cache ring).   The ring
  * write happens after every pair has read its history, which is equivalent
  * because history and window positions never overlap under the invariant. */
 void orc_verify(orc_args *A, int write_ring, int nthreads)

@@ -229,6 +229,120 @@ def test_orthogonal_keys_decouple_the_window():
         np.testing.assert_allclose(o[t, 0], ref, rtol=1e-12, atol=1e-14)
 
 
+# ------------------------------------------------- corrected deltas (d ring)
+
+def test_step_delta_is_the_rank_one_factor():
+    # S_new - e^g S_old = d kh^T: the delta the oracle reports is exactly what
+    # the step adds along the normalised key
+    rng = synth.make_rng(17)
+    for _ in range(5):
+        S = rng.normal(size=(6, 9))
+        k, v = rng.normal(size=9), rng.normal(size=6)
+        g, beta = -abs(rng.normal()), rng.uniform(0.05, 0.95)
+        S1, d = oracle.step_d(S, k, v, g, beta)
+        kh = k / math.sqrt(k @ k + 1e-6)
+        np.testing.assert_allclose(S1 - math.exp(g) * S, np.outer(d, kh), rtol=0, atol=1e-13)
+        np.testing.assert_array_equal(S1, oracle.step(S, k, v, g, beta))
+
+
+def _prefilled_layer_dcache(shape, seed, wp_by_slot, base_by_slot, variant="base"):
+    """Like _prefilled_layer, but the history is committed through one-token
+    d-cache verifies, so the d ring holds what those verifies recorded."""
+    rng = synth.make_rng(seed)
+    p = synth.layer_params(rng, shape, variant)
+    layer = oracle.OracleLayer(shape, p.A_log, p.dt_bias, p.S0)
+    slots = synth.slot_choice(rng, shape)
+    nrec = int(max(wp_by_slot))
+    hist = synth.history_windows(rng, shape, nrec, variant)
+    cur = CursorState.zeros(shape.num_slots)
+    cur.cache_base[:] = base_by_slot
+    for r, (sl, w) in enumerate(zip(helpers.prefill_plan(slots, wp_by_slot, nrec), hist)):
+        cur.write_pos[:] = r
+        layer.verify(cur, sl, helpers.win_f64(w, shape.act), write_ring=True,
+                     fold_flagged=False, T=1, dcache=True)
+    cur.write_pos[:] = wp_by_slot
+    cur.is_flush[:] = 0
+    win = synth.window(rng, shape, variant)
+    return layer, cur, slots, win
+
+
+def _sequence(layer, shape, cur, slot, row, hv, win64):
+    """(keys, values, g, beta, queries, hist, d_ring_hist) of one (row, value head)."""
+    h = hv // (shape.HV // shape.H)
+    hist = clamp_write_pos(cur.write_pos[slot], shape.L, shape.T)
+    ph = [phys(cur.cache_base[slot], j, shape.L) for j in range(hist)]
+    keys = [layer.rawk[slot, h, p] for p in ph]
+    vals = [layer.rawv[slot, hv, p] for p in ph]
+    gs = [layer.g[slot, hv, p] for p in ph]
+    bs = [layer.beta[slot, hv, p] for p in ph]
+    dh = np.array([layer.d[slot, hv, p] for p in ph]).reshape(hist, shape.V)
+    q, k, v, a, b = win64
+    for t in range(shape.T):
+        tok = row * shape.T + t
+        g, beta = oracle.gate(a[tok, hv], b[tok, hv], layer.A_log[hv], layer.dt_bias[hv],
+                              shape.softplus_threshold)
+        keys.append(k[tok, h])
+        vals.append(v[tok, hv])
+        gs.append(g)
+        bs.append(beta)
+    queries = np.stack([q[row * shape.T + t, h] for t in range(shape.T)])
+    return np.stack(keys), np.stack(vals), np.array(gs), np.array(bs), queries, hist, dh
+
+
+@pytest.mark.parametrize("variant", ["base", "low_decay"])
+def test_dcache_route_matches_the_recurrence(variant):
+    # The d ring written by one-token d-cache verifies holds the deltas of the
+    # full system (each depends only on its prefix), the window's deltas match
+    # an independent numpy solve, and the d-cache closed form (history only
+    # through stored deltas, a T x T window solve) reproduces the outputs.
+    shape = _tiny_shape(scale=0.8)
+    wp = np.array([0, 5, 13, 9, 1], dtype=np.int32)
+    base = np.array([3, 14, 9, 0, 15], dtype=np.int32)
+    layer, cur, slots, win = _prefilled_layer_dcache(shape, 23, wp, base, variant)
+    win64 = helpers.win_f64(win, shape.act)
+    o = layer.verify(cur, slots, win64, write_ring=False, fold_flagged=False, dcache=True)
+    dwin = layer.last_dwin
+    worst = {"ring": 0.0, "dwin": 0.0, "out": 0.0, "dw": 0.0}
+    for row, s in enumerate(slots):
+        s = int(s)
+        for hv in range(shape.HV):
+            keys, vals, gs, bs, queries, hist, dh = _sequence(layer, shape, cur, s, row, hv, win64)
+            D = closed_form.deltas(layer.S[s, hv], keys, vals, gs, bs, shape.l2norm_eps)
+            got_w = dwin[row * shape.T:(row + 1) * shape.T, hv]
+            if hist:
+                worst["ring"] = max(worst["ring"], helpers.max_rel(dh, D[:hist]))
+            worst["dwin"] = max(worst["dwin"], helpers.max_rel(got_w, D[hist:]))
+            out, Dw = closed_form.dcache_window(layer.S[s, hv], D[:hist], keys, vals, gs, bs,
+                                               queries, hist, shape.scale, shape.l2norm_eps)
+            worst["out"] = max(worst["out"], helpers.max_rel(o[row * shape.T:(row + 1) * shape.T, hv], out))
+            worst["dw"] = max(worst["dw"], helpers.max_rel(got_w, Dw))
+    assert max(worst.values()) < 1e-12, worst
+
+
+def test_dcache_ring_write_lands_at_write_pos():
+    shape = _tiny_shape()
+    wp = np.array([3, 0, 8, 12, 5], np.int32)
+    layer, cur, slots, win = _prefilled_layer_dcache(shape, 27, wp, np.array([1, 4, 15, 7, 0], np.int32))
+    slots = slots.copy()
+    slots[1] = -1                                   # a padding row writes nothing
+    before = layer.d.copy()
+    win64 = helpers.win_f64(win, shape.act)
+    o_plain = layer.verify(cur, slots, win64, write_ring=False, fold_flagged=False)
+    o = layer.verify(cur, slots, win64, write_ring=True, fold_flagged=False, dcache=True)
+    assert np.array_equal(o, o_plain, equal_nan=True)   # the d ring changes no output
+    written = np.zeros(layer.d.shape[:3], bool)
+    for row, s in enumerate(slots):
+        if s < 0:
+            continue
+        for t in range(shape.T):
+            p = phys(cur.cache_base[s], int(cur.write_pos[s]) + t, shape.L)
+            written[s, :, p] = True
+            np.testing.assert_array_equal(layer.d[s, :, p], layer.last_dwin[row * shape.T + t])
+    same = ~written
+    assert np.array_equal(np.isnan(layer.d[same]), np.isnan(before[same]))
+    np.testing.assert_array_equal(np.nan_to_num(layer.d[same]), np.nan_to_num(before[same]))
+
+
 # ------------------------------------------------------- structural invariants
 
 def test_causality_later_tokens_do_not_change_earlier_outputs():
