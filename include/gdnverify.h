@@ -126,6 +126,48 @@ int gdn_spec_verify_ring(const gdn_shape *shape,
                          void *o, void *stream);
 
 /*
+ * gdn_spec_verify_dcache -- the verify step through a ring of corrected
+ * deltas (the first-generation ring of replayssm(B)SpecDecode §1.1 table,
+ * which caches d, k and g per committed token; §12.6 defines the corrected
+ * delta d = beta (v - e^g S k_hat), the rank-1 factor of a step).
+ *
+ * Same arguments, outputs and side effects as gdn_spec_verify_ring, plus
+ *    ring_d  [num_slots, HV, L, V] fp32, caller-owned (gdn_dring_bytes).
+ * The committed history enters only through ring_d: record j's stored delta
+ * at physical position (cache_base + j) & (L-1), together with its raw key
+ * and gate from the raw ring (its raw value is not read).  The window's
+ * deltas follow from a T x T unit lower-triangular system, and the outputs
+ * equal gdn_spec_verify_ring's up to rounding.
+ * write_ring = 1: besides the raw records, ring_d[s, hv, p, :] receives the
+ *   window token's corrected delta at p = (cache_base + write_pos + t) & (L-1).
+ *   Nothing else in ring_d is written.
+ * Precondition: for every unflagged row, ring_d holds at logical positions
+ *   0..write_pos-1 the deltas recorded by d-cache verifies (with
+ *   write_ring = 1) since the slot's last fold or reset.  A delta depends on
+ *   the checkpoint it was formed against, so a slot folded for any other
+ *   reason must be reset before its next d-cache verify.  Flagged rows are
+ *   folded (fold_flagged = 1) from the raw records and verified with an empty
+ *   history, so they need no stored deltas.
+ * Returns GDN_EUNSUPPORTED where the kernel's LDS would exceed 160 KB
+ * (never for the shapes gdn_validate_shape accepts).  ring_d must not alias o.
+ */
+int gdn_spec_verify_dcache(const gdn_shape *shape,
+                           const void *q, const void *k, const void *v,
+                           const void *a, const void *b,
+                           const float *A_log, const float *dt_bias,
+                           float *S, const int32_t *slot_idx,
+                           const int32_t *write_pos, const int32_t *cache_base,
+                           const int32_t *is_flush,
+                           void *ring_rawk, void *ring_rawv,
+                           float *ring_g, float *ring_beta, float *ring_d,
+                           int write_ring, int fold_flagged,
+                           void *o, void *stream);
+
+/* Bytes of the d ring of gdn_spec_verify_dcache: num_slots*HV*L*V*4
+ * (0 for an invalid shape). */
+size_t gdn_dring_bytes(const gdn_shape *shape);
+
+/*
  * gdn_exact_fold -- closed-loop exact fold of committed ring records into the
  * checkpoint (PR #28695 summary, implementation item 3: sequential replay from
  * the raw inputs, consistent with the recurrent update; replayssm(B)SpecDecode

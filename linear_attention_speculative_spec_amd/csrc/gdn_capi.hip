@@ -141,6 +141,52 @@ int gdn_spec_verify_ring(const gdn_shape* shape, const void* q, const void* k, c
     return status_of(launch_verify(sh, w, S, slot_idx, c, r, write_ring ? 1 : 0, o, strm));
 }
 
+int gdn_spec_verify_dcache(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const void* a, const void* b, const float* A_log,
+                           const float* dt_bias, float* S, const int32_t* slot_idx,
+                           const int32_t* write_pos, const int32_t* cache_base,
+                           const int32_t* is_flush, void* ring_rawk, void* ring_rawv,
+                           float* ring_g, float* ring_beta, float* ring_d, int write_ring,
+                           int fold_flagged, void* o, void* stream)
+{
+    int st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape& sh = *shape;
+    if (dcache_lds_bytes(sh) > max_lds_bytes())
+        return GDN_EUNSUPPORTED;
+    const size_t eb = act_bytes(sh);
+    if (!ok_ptr(q, 16) || !ok_ptr(k, 16) || !ok_ptr(v, 16) || !ok_ptr(a, eb) || !ok_ptr(b, eb) ||
+        !ok_ptr(A_log, 4) || !ok_ptr(dt_bias, 4) || !ok_ptr(S, 16) || !ok_ptr(slot_idx, 4) ||
+        !ok_ptr(write_pos, 4) || !ok_ptr(cache_base, 4) || !ok_ptr(is_flush, 4) ||
+        !ok_ptr(ring_rawk, 16) || !ok_ptr(ring_rawv, 16) || !ok_ptr(ring_g, 4) ||
+        !ok_ptr(ring_beta, 4) || !ok_ptr(ring_d, 16) || !ok_ptr(o, 16))
+        return GDN_EINVAL;
+    if (o == q || o == k || o == v || o == S || o == ring_d)
+        return GDN_EINVAL;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    const WindowPtrs w = {q, k, v, a, b, A_log, dt_bias};
+    const CursorPtrs c = {write_pos, cache_base, is_flush};
+    const RingPtrs r = {ring_rawk, ring_rawv, ring_g, ring_beta};
+    if (fold_flagged) {
+        // launch 1: flagged rows advance their checkpoint exactly (raw records)
+        st = status_of(launch_fold(sh, 1, S, r, slot_idx, c, 1, strm));
+        if (st != GDN_OK)
+            return st;
+    }
+    // launch 2: outputs through the stored deltas; the window's deltas recorded
+    return status_of(launch_dcache_verify(sh, w, S, slot_idx, c, r, ring_d, write_ring ? 1 : 0,
+                                          o, strm));
+}
+
+size_t gdn_dring_bytes(const gdn_shape* shape)
+{
+    if (check_shape(shape) != GDN_OK)
+        return 0;
+    const gdn_shape& s = *shape;
+    return static_cast<size_t>(s.num_slots) * s.HV * s.L * s.V * 4;
+}
+
 int gdn_exact_fold(const gdn_shape* shape, int num_layers, float* S, const void* ring_rawk,
                    const void* ring_rawv, const float* ring_g, const float* ring_beta,
                    const int32_t* slot_idx, const int32_t* write_pos, const int32_t* cache_base,

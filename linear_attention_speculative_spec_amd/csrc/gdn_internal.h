@@ -41,6 +41,14 @@ hipError_t launch_verify(const gdn_shape& sh, const WindowPtrs& w, const float* 
                          const int32_t* slot_idx, const CursorPtrs& c, const RingPtrs& r,
                          int write_ring, void* o, hipStream_t stream);
 
+// The d-cache verify: history through stored corrected deltas ring_d
+// [num_slots, HV, L, V] fp32; records the window's deltas there (write_ring).
+size_t dcache_lds_bytes(const gdn_shape& sh);
+
+hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const float* S,
+                                const int32_t* slot_idx, const CursorPtrs& c, const RingPtrs& r,
+                                float* ring_d, int write_ring, void* o, hipStream_t stream);
+
 hipError_t launch_fold(const gdn_shape& sh, int num_layers, float* S, const RingPtrs& r,
                        const int32_t* slot_idx, const CursorPtrs& c, int only_flagged,
                        hipStream_t stream);

@@ -22,6 +22,7 @@ EXPORTED = (
     "gdn_spec_verify_ring", "gdn_exact_fold", "gdn_advance_cursors", "gdn_reset_cursors",
     "gdn_recurrent_verify_snapshot", "gdn_snapshot_commit", "gdn_ring_bytes",
     "gdn_snapshot_bytes", "gdn_validate_shape", "gdn_status_str",
+    "gdn_spec_verify_dcache", "gdn_dring_bytes",
 )
 
 
@@ -67,12 +68,13 @@ def lib():
                                "(python -m linear_attention_speculative_spec_amd._build)")
         L = ctypes.CDLL(_LIB_PATH)
         L.gdn_spec_verify_ring.argtypes = [_sp] + [_vp] * 16 + [_i, _i, _vp, _vp]
+        L.gdn_spec_verify_dcache.argtypes = [_sp] + [_vp] * 17 + [_i, _i, _vp, _vp]
         L.gdn_exact_fold.argtypes = [_sp, _i] + [_vp] * 9 + [_i, _vp]
         L.gdn_advance_cursors.argtypes = [_sp] + [_vp] * 6
         L.gdn_reset_cursors.argtypes = [_sp, _vp, ctypes.c_int32, ctypes.c_int32] + [_vp] * 4
         L.gdn_recurrent_verify_snapshot.argtypes = [_sp] + [_vp] * 17 + [_i, _vp]
         L.gdn_snapshot_commit.argtypes = [_sp] + [_vp] * 5
-        for fn in ("gdn_spec_verify_ring", "gdn_exact_fold", "gdn_advance_cursors",
+        for fn in ("gdn_spec_verify_ring", "gdn_spec_verify_dcache", "gdn_exact_fold", "gdn_advance_cursors",
                    "gdn_reset_cursors", "gdn_recurrent_verify_snapshot", "gdn_snapshot_commit",
                    "gdn_validate_shape"):
             getattr(L, fn).restype = ctypes.c_int
@@ -81,6 +83,8 @@ def lib():
         L.gdn_ring_bytes.restype = ctypes.c_size_t
         L.gdn_snapshot_bytes.argtypes = [_sp]
         L.gdn_snapshot_bytes.restype = ctypes.c_size_t
+        L.gdn_dring_bytes.argtypes = [_sp]
+        L.gdn_dring_bytes.restype = ctypes.c_size_t
         L.gdn_status_str.argtypes = [_i]
         L.gdn_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -171,6 +175,24 @@ def gdn_spec_verify_ring(shape, q, k, v, a, b, A_log, dt_bias, S, slot_idx, writ
     _check("gdn_spec_verify_ring", st)
 
 
+def gdn_spec_verify_dcache(shape, q, k, v, a, b, A_log, dt_bias, S, slot_idx, write_pos,
+                           cache_base, is_flush, ring_rawk, ring_rawv, ring_g, ring_beta,
+                           ring_d, write_ring, fold_flagged, o, stream=None):
+    _window_checks(shape, q, k, v, a, b, A_log, dt_bias)
+    _need("S", S, shape.num_slots * shape.HV * shape.V * shape.K, torch.float32)
+    _need("slot_idx", slot_idx, shape.B, torch.int32)
+    _cursor_checks(shape, write_pos, cache_base, is_flush)
+    _ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta)
+    _need("ring_d", ring_d, shape.num_slots * shape.HV * shape.L * shape.V, torch.float32)
+    _need("o", o, shape.B * shape.T * shape.HV * shape.V, _act_dtype(shape))
+    st = lib().gdn_spec_verify_dcache(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+        _ptr(dt_bias), _ptr(S), _ptr(slot_idx), _ptr(write_pos), _ptr(cache_base),
+        _ptr(is_flush), _ptr(ring_rawk), _ptr(ring_rawv), _ptr(ring_g), _ptr(ring_beta),
+        _ptr(ring_d), int(write_ring), int(fold_flagged), _ptr(o), _stream(stream))
+    _check("gdn_spec_verify_dcache", st)
+
+
 def gdn_exact_fold(shape, num_layers, S, ring_rawk, ring_rawv, ring_g, ring_beta, slot_idx,
                    write_pos, cache_base, is_flush, only_flagged, stream=None):
     _need("S", S, num_layers * shape.num_slots * shape.HV * shape.V * shape.K, torch.float32)
@@ -240,6 +262,10 @@ def gdn_ring_bytes(shape) -> int:
 
 def gdn_snapshot_bytes(shape) -> int:
     return int(lib().gdn_snapshot_bytes(ctypes.byref(shape)))
+
+
+def gdn_dring_bytes(shape) -> int:
+    return int(lib().gdn_dring_bytes(ctypes.byref(shape)))
 
 
 def gdn_validate_shape(shape) -> int:

@@ -75,6 +75,13 @@ class GpuLayer:
     def ring(self):
         return self.rawk, self.rawv, self.g, self.beta
 
+    def verify_dcache(self, cur, slot_idx, win: DevWindow, o, write_ring=1, fold_flagged=1,
+                      gs=None):
+        gv.gdn_spec_verify_dcache(gs or self.gs, win.q, win.k, win.v, win.a, win.b, self.A_log,
+                                  self.dt_bias, self.S, slot_idx, cur[0], cur[1], cur[2],
+                                  self.rawk, self.rawv, self.g, self.beta, self.rd, write_ring,
+                                  fold_flagged, o)
+
     def verify(self, cur, slot_idx, win: DevWindow, o, write_ring=1, fold_flagged=1, gs=None):
         gv.gdn_spec_verify_ring(gs or self.gs, win.q, win.k, win.v, win.a, win.b, self.A_log,
                                 self.dt_bias, self.S, slot_idx, cur[0], cur[1], cur[2],
@@ -101,7 +108,8 @@ class Pair:
     """A GPU layer and an oracle layer built from one seed, rings pre-filled."""
 
     def __init__(self, shape: synth.LayerShape, seed: int, variant: str = "base",
-                 wp_by_slot=None, base_by_slot=None, slots=None, oracle_rows=None):
+                 wp_by_slot=None, base_by_slot=None, slots=None, oracle_rows=None,
+                 dcache=False):
         require_gpu()
         self.shape = shape
         self.act = shape.act
@@ -115,6 +123,15 @@ class Pair:
         base = cd.cache_base if base_by_slot is None else np.asarray(base_by_slot, np.int32)
         self.template = synth.ring_garbage_template(rng, shape)
         self.gpu = GpuLayer(shape, self.params, self.template)
+        self.dcache = dcache
+        if dcache:
+            # d ring of NaN payloads from a generator of its own (the main
+            # stream stays as without it)
+            drng = synth.make_rng(seed + 7919)
+            n = shape.num_slots * shape.HV * shape.L * shape.V
+            bits = (np.uint32(0x7FC00000) | drng.integers(1, 0x3FFFFF, size=n, dtype=np.uint32))
+            self.d_template = bits.astype(np.uint32).reshape(shape.num_slots, shape.HV, shape.L, shape.V)
+            self.gpu.rd = torch.from_numpy(self.d_template.view(np.float32).copy()).to(DEV)
         # oracle: only the rows asked for (all by default), slots renumbered
         self.orows = np.arange(shape.B) if oracle_rows is None else np.asarray(oracle_rows)
         osh = shape.replace(B=len(self.orows), num_slots=len(self.orows))
@@ -135,12 +152,17 @@ class Pair:
         plan = helpers.prefill_plan(self.slots, wp, nrec)
         for r, (sl, w) in enumerate(zip(plan, hist)):
             cur_g.write_pos[:] = r
-            self.gpu.verify(dev_cursors(cur_g), dev_i32(sl), DevWindow(w, self.act), scratch,
-                            write_ring=1, fold_flagged=0, gs=gs1)
+            verify = self.gpu.verify_dcache if dcache else self.gpu.verify
+            verify(dev_cursors(cur_g), dev_i32(sl), DevWindow(w, self.act), scratch,
+                   write_ring=1, fold_flagged=0, gs=gs1)
             cur_o.write_pos[:] = r
             osl = np.where(sl[self.orows] >= 0, self.oslots, -1).astype(np.int32)
             wo = helpers.window_rows(w, self.orows, 1)
-            self.orc.write_ring(cur_o, osl, helpers.win_f64(wo, self.act), T=1)
+            if dcache:
+                self.orc.verify(cur_o, osl, helpers.win_f64(wo, self.act), write_ring=True,
+                                fold_flagged=False, T=1, dcache=True)
+            else:
+                self.orc.write_ring(cur_o, osl, helpers.win_f64(wo, self.act), T=1)
         torch.cuda.synchronize()
         self.cur = CursorState(wp.copy(), base.copy(),
                                (wp + 2 * shape.max_spec > shape.L).astype(np.int32))
@@ -155,10 +177,12 @@ class Pair:
     def window(self) -> synth.Window:
         return synth.window(self.rng, self.shape, self.variant)
 
-    def oracle_verify(self, win: synth.Window, write_ring=True, fold_flagged=True, pairs=None):
+    def oracle_verify(self, win: synth.Window, write_ring=True, fold_flagged=True, pairs=None,
+                      dcache=False):
         wo = helpers.window_rows(win, self.orows, self.shape.T)
         return self.orc.verify(self.ocur, self.oslots, helpers.win_f64(wo, self.act),
-                               write_ring=write_ring, fold_flagged=fold_flagged, pairs=pairs)
+                               write_ring=write_ring, fold_flagged=fold_flagged, pairs=pairs,
+                               dcache=dcache)
 
     def gpu_out_rows(self, o: torch.Tensor) -> np.ndarray:
         """GPU outputs of the oracle's rows, widened to float64."""

@@ -97,6 +97,14 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert L.gdn_reset_cursors(ctypes.byref(sh), good, -1, 0, good, good, good, n) == gv.GDN_EINVAL
     assert L.gdn_advance_cursors(ctypes.byref(sh), good, n, good, good, good, n) == gv.GDN_EINVAL
     assert L.gdn_snapshot_commit(ctypes.byref(sh), good, good, n, good, n) == gv.GDN_EINVAL
+    # the d-cache verify: null ring_d, misaligned ring_d, o aliasing ring_d
+    args = [good] * 17
+    args[16] = n
+    assert L.gdn_spec_verify_dcache(ctypes.byref(sh), *args, 1, 1, ctypes.c_void_p(2 << 20), n) == gv.GDN_EINVAL
+    args[16] = bad
+    assert L.gdn_spec_verify_dcache(ctypes.byref(sh), *args, 1, 1, ctypes.c_void_p(2 << 20), n) == gv.GDN_EINVAL
+    args = [ctypes.c_void_p((3 + i) << 20) for i in range(17)]
+    assert L.gdn_spec_verify_dcache(ctypes.byref(sh), *args, 1, 1, args[16], n) == gv.GDN_EINVAL
 
 
 def test_footprints():
@@ -106,6 +114,8 @@ def test_footprints():
     assert gv.gdn_ring_bytes(sh) == 512 * 64 * rec
     assert gv.gdn_snapshot_bytes(sh) == 256 * 4 * 32 * 128 * 128 * 4
     assert gv.gdn_snapshot_bytes(sh) > 5 * gv.gdn_ring_bytes(sh)
+    # the d ring: one fp32 delta row per (slot, value head, record)
+    assert gv.gdn_dring_bytes(sh) == 512 * 32 * 64 * 128 * 4
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

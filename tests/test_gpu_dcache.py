@@ -1,0 +1,169 @@
+"""GPU parity of the d-cache verify (gdn_spec_verify_dcache) against the oracle.
+
+The verify reads the committed history through a ring of corrected deltas
+that earlier d-cache verifies recorded; the oracle records the deltas of its
+own recurrence (d = beta (v - e^g S k_hat)) in a d ring of its own.  Bars:
+outputs, recorded deltas and folded states within max|x-ref|/max|ref| of 2e-3
+(fp32 activations) or 3e-2 (bf16); raw ring bits and cursors exact; d ring
+entries outside the written windows keep the garbage template's bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.cursors import advance
+from linear_attention_speculative_spec_amd import gdnverify as gv
+from linear_attention_speculative_spec_amd import synth
+
+import helpers
+from gpu_harness import DevWindow, Pair, dev_i32, host_bits, host_cursors, host_f64
+from test_gpu_parity import SWEEP, prefill_tracker
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.ACT_F32: 2e-3, synth.ACT_BF16: 3e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_d_ring(P: Pair, tr, tol):
+    """Written d ring entries of the oracle's rows against the oracle's d ring;
+    every entry never written still holds the template bits."""
+    gslots = P.slots[P.orows]
+    rd = host_f64(P.gpu.rd)
+    w = tr.written[gslots]                       # [rows, HV, L]
+    err = helpers.max_rel(rd[gslots][w], P.orc.d[w]) if w.any() else 0.0
+    assert err <= tol, err
+    bits = host_bits(P.gpu.rd)
+    un = ~tr.written
+    assert np.array_equal(bits[un], P.d_template[un]), "d ring written outside the windows"
+    return err
+
+
+def run_dcache_lifecycle(shape, seed, steps, variant="base", wp_by_slot=None, oracle_rows=None):
+    P = Pair(shape, seed, variant, wp_by_slot=wp_by_slot, oracle_rows=oracle_rows, dcache=True)
+    tol = TOL[shape.act]
+    tr = prefill_tracker(P)
+    check_d_ring(P, tr, tol)
+    accepts = synth.accept_counts(P.rng, shape.B, shape.T, steps)
+    gslots = P.slots[P.orows]
+    worst = {"o": 0.0, "S": 0.0, "d": 0.0}
+    flushes = 0
+    for i in range(steps):
+        win = P.window()
+        o = P.gpu.new_out()
+        flushes += int(P.cur.is_flush[P.slots].sum())
+        P.gpu.verify_dcache(P.dcur, P.dslots, DevWindow(win, shape.act), o)
+        ref = P.oracle_verify(win, dcache=True)
+        tr.record(P.slots, P.cur, win, shape.T)
+        err = helpers.max_rel(P.gpu_out_rows(o), ref)
+        worst["o"] = max(worst["o"], err)
+        assert err <= tol, (i, err)
+        acc = accepts[i]
+        gv.gdn_advance_cursors(P.gpu.gs, P.dslots, dev_i32(acc), *P.dcur)
+        advance(P.cur, P.slots, acc, shape.L, shape.T, shape.max_spec)
+        advance(P.ocur, P.oslots, acc[P.orows], shape.L, shape.T, shape.max_spec)
+        got = host_cursors(P.dcur)
+        for name in ("write_pos", "cache_base", "is_flush"):
+            assert np.array_equal(getattr(got, name), getattr(P.cur, name)), (name, i)
+        serr = helpers.max_rel(host_f64(P.gpu.S)[gslots], P.orc.S)
+        worst["S"] = max(worst["S"], serr)
+        assert serr <= tol, (i, serr)
+        if i % 4 == 3 or i == steps - 1:
+            worst["d"] = max(worst["d"], check_d_ring(P, tr, tol))
+    tr.check(P.gpu, P.orc, gslots)
+    say(f"d-cache lifecycle {shape.act} B={shape.B} T={shape.T} K={shape.K} V={shape.V} "
+        f"L={shape.L} {variant}: steps={steps} flushes={flushes} "
+        + " ".join(f"max_rel({k})={v:.2e}" for k, v in worst.items()))
+    return P, flushes
+
+
+@pytest.mark.parametrize("variant", ["base", "low_decay", "beta_high"])
+def test_dcache_tiny_f32_lifecycle_40_steps(variant):
+    shape = synth.CONFIGS["tiny_f32"]
+    wp = np.full(shape.num_slots, 5, np.int32)
+    _, flushes = run_dcache_lifecycle(shape, 1000, 40, variant, wp_by_slot=wp)
+    assert flushes >= 2
+
+
+@pytest.mark.parametrize("variant", ["base", "low_decay"])
+def test_dcache_qwen3next_b32_lifecycle(variant):
+    shape = synth.CONFIGS["qwen3next_b32"]
+    run_dcache_lifecycle(shape, 1001, 24, variant, oracle_rows=np.arange(0, 32, 3))
+
+
+def test_dcache_long_window_t8_lifecycle_reduced_batch():
+    shape = synth.CONFIGS["long_window_t8"].replace(B=8, num_slots=16)
+    _, flushes = run_dcache_lifecycle(shape, 1003, 60, "low_decay")
+    assert flushes >= 4
+
+
+@pytest.mark.parametrize("kw", SWEEP, ids=[f"K{d['K']}V{d['V']}T{d['T']}L{d['L']}{d['act']}" for d in SWEEP])
+def test_dcache_shape_sweep(kw):
+    shape = synth.LayerShape(**kw, scale=0.5)
+    rng = synth.make_rng(3100 + kw["K"] + kw["V"])
+    wp = rng.integers(0, shape.L - shape.T + 1, size=shape.num_slots).astype(np.int32)
+    wp[:2] = [0, shape.L - shape.T]
+    run_dcache_lifecycle(shape, 3100 + kw["L"], 6, "low_decay", wp_by_slot=wp)
+
+
+def test_dcache_agrees_with_the_raw_replay_verify():
+    # one seed, two layers: rings pre-filled by the raw-replay verify and by
+    # the d-cache verify write the same raw records bit for bit, and the two
+    # verifies of the same window agree within the activation tolerance
+    shape = synth.CONFIGS["qwen3next_b32"]
+    Pr = Pair(shape, 1500, "low_decay", oracle_rows=[0])
+    Pd = Pair(shape, 1500, "low_decay", oracle_rows=[0], dcache=True)
+    for a, b in zip(Pr.gpu.ring(), Pd.gpu.ring()):
+        assert np.array_equal(host_bits(a), host_bits(b))
+    worst = 0.0
+    for i in range(6):
+        win = Pr.window()
+        assert np.array_equal(win.q, Pd.window().q)
+        orr, od = Pr.gpu.new_out(), Pd.gpu.new_out()
+        Pr.gpu.verify(Pr.dcur, Pr.dslots, DevWindow(win, shape.act), orr)
+        Pd.gpu.verify_dcache(Pd.dcur, Pd.dslots, DevWindow(win, shape.act), od)
+        err = helpers.max_rel(host_f64(od), host_f64(orr))
+        worst = max(worst, err)
+        assert err <= TOL[shape.act], (i, err)
+        for a, b in zip(Pr.gpu.ring(), Pd.gpu.ring()):
+            assert np.array_equal(host_bits(a), host_bits(b)), i
+        # both folds run on identical raw rings: identical checkpoints
+        assert np.array_equal(host_bits(Pr.gpu.S), host_bits(Pd.gpu.S)), i
+        acc = Pr.rng.integers(0, shape.T + 1, size=shape.B).astype(np.int32)
+        Pd.rng.integers(0, shape.T + 1, size=shape.B)
+        for P in (Pr, Pd):
+            gv.gdn_advance_cursors(P.gpu.gs, P.dslots, dev_i32(acc), *P.dcur)
+    say(f"d-cache vs raw replay, 6 steps: max_rel(o)={worst:.2e}")
+
+
+def test_dcache_ring_write_is_a_side_channel_and_padding_rows_are_inert():
+    shape = synth.CONFIGS["qwen3next_b32"]
+    P = Pair(shape, 2600, dcache=True, oracle_rows=[0])
+    slots = P.slots.copy()
+    slots[[2, 11]] = [-1, shape.num_slots + 3]
+    dsl = dev_i32(slots)
+    win = DevWindow(P.window(), shape.act)
+    S0 = P.gpu.S.clone()
+    rd0 = host_bits(P.gpu.rd)
+    outs = []
+    for wr in (0, 1):
+        P.gpu.S.copy_(S0)
+        o = P.gpu.new_out()
+        P.gpu.verify_dcache(P.dcur, dsl, win, o, write_ring=wr, fold_flagged=1)
+        outs.append(host_bits(o))
+        if wr == 0:
+            assert np.array_equal(host_bits(P.gpu.rd), rd0), "d ring written with write_ring = 0"
+    assert np.array_equal(outs[0], outs[1])
+    sentinel = host_bits(P.gpu.new_out())
+    for r in (2, 11):
+        rows = slice(r * shape.T, (r + 1) * shape.T)
+        assert np.array_equal(outs[1][rows], sentinel[rows])
+    # the padding rows' former slots, now referenced by no row, kept their d ring rows
+    rd1 = host_bits(P.gpu.rd)
+    for r in (2, 11):
+        assert np.array_equal(rd1[P.slots[r]], rd0[P.slots[r]]), r
