@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-snapshot", action="store_true")
+    ap.add_argument("--no-dcache", action="store_true",
+                    help="skip the comparison with the d-cache verify")
     ap.add_argument("--no-fold-every-commit", action="store_true",
                     help="skip the comparison with the fold-every-commit design")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -78,6 +80,23 @@ def verify_alg_bytes(sh, hist: np.ndarray) -> int:
     out = B * T * sh.HV * sh.V * eb
     ring_w = B * T * record_bytes(sh)
     hist_r = int(hist.sum()) * record_bytes(sh)
+    return s0 + hist_r + win + out + ring_w + B * 16
+
+
+def dcache_alg_bytes(sh, hist: np.ndarray) -> int:
+    """Bytes the d-cache verify must move for one call (each counted once).
+
+    As the raw-replay verify, except that a committed record is read as its
+    key, gate and fp32 corrected delta (not its raw value), and the window's
+    deltas are written beside its raw records."""
+    eb = 2 if sh.act == "bf16" else 4
+    B, T = sh.B, sh.T
+    s0 = B * sh.HV * sh.V * sh.K * 4
+    win = B * T * (2 * sh.H * sh.K + sh.HV * sh.V + 2 * sh.HV) * eb
+    out = B * T * sh.HV * sh.V * eb
+    dvec = sh.HV * sh.V * 4
+    ring_w = B * T * (record_bytes(sh) + dvec)
+    hist_r = int(hist.sum()) * (sh.H * sh.K * eb + sh.HV * 8 + dvec)
     return s0 + hist_r + win + out + ring_w + B * 16
 
 
@@ -363,6 +382,64 @@ def main():
         log(f"[bench] fold every commit: step {f_step:.1f} us")
         del rkf, rvf, rgf, rbf, Sf
 
+    if not args.no_dcache:
+        # The d-cache design: the verify reads the committed history through
+        # the corrected deltas earlier verifies recorded.  Same checkpoint,
+        # cursors, windows and accept counts; its own rings, pre-filled by
+        # one-token d-cache verifies of history records drawn the same way.
+        rkd = torch.zeros_like(rawk)
+        rvd = torch.zeros_like(rawv)
+        rgd = torch.zeros_like(rg)
+        rbd = torch.zeros_like(rb)
+        rdd = torch.zeros(sh.num_slots, sh.HV, sh.L, sh.V, dtype=torch.float32, device=dev)
+        Sd = f32(params.S0)
+        hw = synth.history_windows(synth.make_rng(args.seed + 1), sh, n_hist)
+        for r, w in enumerate(hw):
+            sl = np.where(cd.write_pos[slots] > r, slots, -1).astype(np.int32)
+            gv.gdn_spec_verify_dcache(gs1, *[bf(x) for x in (w.q, w.k, w.v, w.a, w.b)], A_log,
+                                      dt_bias, Sd, i32(sl), i32(np.full(sh.num_slots, r)), base_d,
+                                      zeros, rkd, rvd, rgd, rbd, rdd, 1, 0, scratch)
+        del hw
+        curd = [i32(wp0), i32(cd.cache_base), i32(fl0)]
+
+        def step_d(i, ev=None):
+            w = wins[i % n_pool]
+            if ev is not None:
+                ev[0].record()
+            gv.gdn_exact_fold(gs, 1, Sd, rkd, rvd, rgd, rbd, dslots, *curd, 1)
+            if ev is not None:
+                ev[1].record()
+            gv.gdn_spec_verify_dcache(gs, *w, A_log, dt_bias, Sd, dslots, *curd, rkd, rvd, rgd,
+                                      rbd, rdd, 1, 0, o)
+            if ev is not None:
+                ev[2].record()
+            gv.gdn_advance_cursors(gs, dslots, acc_d[i], *curd)
+
+        for i in range(args.warmup):
+            step_d(i)
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for j in range(args.steps):
+            step_d(args.warmup + j, evd[j])
+        e1.record()
+        torch.cuda.synchronize()
+        d_step = e0.elapsed_time(e1) / args.steps * 1e3
+        d_ver = float(np.mean([e[1].elapsed_time(e[2]) for e in evd]) * 1e3)
+        dbytes = float(np.mean([dcache_alg_bytes(sh, hist_per_step[i]) for i in timed]))
+        result["dcache"] = {
+            "step_us": d_step,
+            "verify_us": d_ver,
+            "fold_us": float(np.mean([e[0].elapsed_time(e[1]) for e in evd]) * 1e3),
+            "alg_bytes_per_launch": dbytes,
+            "achieved_GBs": dbytes / (d_ver * 1e-6) / 1e9,
+            "draft_tokens_per_s": tokens / (d_step * 1e-6),
+            "dring_bytes_per_layer": gv.gdn_dring_bytes(gs)}
+        log(f"[bench] d-cache: step {d_step:.1f} us, verify {d_ver:.1f} us "
+            f"({dbytes / (d_ver * 1e-6) / 1e9:.0f} GB/s)")
+        del rkd, rvd, rgd, rbd, rdd, Sd
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, args.seed, args.cpu_seconds)
 
@@ -373,19 +450,19 @@ COPY_BYTES = 256 << 20
 PROFILE_CMDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/kt -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --no-fold-every-commit --no-dcache "
     "--copy-calibration "
     "> $R/gpurun_out/prof/kt.log 2>&1",
     "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
-    "--copy-calibration",
+    "--no-dcache --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
-    "--copy-calibration",
+    "--no-dcache --copy-calibration",
     "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
     "SQ_INSTS_VALU_MFMA_BF16 SQ_INSTS_VALU_MFMA_F32 GRBM_GUI_ACTIVE -d $R/gpurun_out/prof/mfma -o run "
     "--output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot "
-    "--no-fold-every-commit",
+    "--no-fold-every-commit --no-dcache",
     "cd $R && python3 bench.py --summarize-profile gpurun_out/prof",
 ]
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA peaks of the part

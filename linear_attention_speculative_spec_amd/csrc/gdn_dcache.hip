@@ -48,6 +48,7 @@ constexpr int kDcThreads = 64 * kDcWaves;
 constexpr int kDcRows = 128;          // value rows per workgroup (16 per wave)
 constexpr int kDcGroups = kDcThreads / kDcRows;   // thread groups over the history
 constexpr int kTMax = 16;             // window tokens at most (max_spec_len <= 16)
+constexpr int kDPre = 16;             // stored deltas per thread loaded at the start
 constexpr float kLog2eDc = 1.4426950408889634f;
 
 struct DcParams {
@@ -102,8 +103,12 @@ __device__ __forceinline__ float act_at(const void* base, size_t i)
 
 }  // namespace
 
-template <class Act, int K>
-__global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcParams p)
+// TM: window tokens at most for this instantiation (4, 8 or 16): the per-row
+// register arrays are sized by it.  Two workgroups per compute unit (128
+// VGPRs) up to K = 128; K = 256 holds twice the checkpoint registers and runs
+// one.
+template <class Act, int K, int TM>
+__global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_kernel(const DcParams p)
 {
     extern __shared__ __align__(16) float sm[];
     float* Xs = sm + p.o_x;        // [PC][KX] normalised window keys, then queries
@@ -140,6 +145,24 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
 #pragma unroll
     for (int i = 0; i < K / 16; ++i)
         sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + (i & 1) * 8 * K + (i >> 1) * 32));
+    // the stored deltas this thread sums in step 4 (records grp + kDcGroups m,
+    // the first kDPre of them), issued now so their latency hides behind the
+    // staging; indices past the history are clamped to a valid record and
+    // skipped in step 4
+    const int grp = tid / kDcRows, vr = tid % kDcRows;   // (wave-uniform grp)
+    const float* dring = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v0 + vr;
+    float dpre[kDPre];
+#pragma unroll
+    for (int m = 0; m < kDPre; ++m)
+        dpre[m] = 0.0f;
+    if (hist > 0 && vr < BV) {
+#pragma unroll
+        for (int m = 0; m < kDPre; ++m) {
+            const int j = grp + kDcGroups * m;
+            const int jc = j < hist ? j : hist - 1;
+            dpre[m] = dring[static_cast<size_t>((base + jc) & (L - 1)) * V];
+        }
+    }
 
     // window keys (columns 0..TP-1) and queries (TP..2TP-1), normalised; one
     // wave per column, zero columns past T
@@ -204,38 +227,51 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
     }
     // ---- 2b. dot products of every record's key with the window columns:
     // P[j][c] = kh_j . Xs[c] (history keys normalised here, window keys are
-    // the normalised columns themselves)
-    for (int task = tid; task < n * PC; task += kDcThreads) {
+    // the normalised columns themselves).  Four lanes share a product, each
+    // over a quarter of the key with all its loads issued first, and meet by
+    // quad swaps.
+    constexpr int KQ = K / 4;
+    for (int t4 = tid; t4 < n * PC * 4; t4 += kDcThreads) {
+        const int sub = t4 & 3, task = t4 >> 2;
         const int j = task / PC, c = task % PC;
-        float acc = 0.0f;
+        const float* xc = Xs + c * p.KX + sub * KQ;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (j < hist) {
             const int ph = (base + j) & (L - 1);
-            const typename Act::storage* kr =
-                static_cast<const typename Act::storage*>(p.rawk) + ((static_cast<size_t>(s) * H + h) * L + ph) * K;
-            float ss = 0.0f;
-#pragma unroll 4
-            for (int e = 0; e < K; e += 4) {
-                const f32x4 kv = load4<Act>(kr + e);
-                const f32x4 xv = *reinterpret_cast<const f32x4*>(Xs + c * p.KX + e);
+            const typename Act::storage* kr = static_cast<const typename Act::storage*>(p.rawk) +
+                                              ((static_cast<size_t>(s) * H + h) * L + ph) * K + sub * KQ;
+            f32x4 kv[KQ / 4];
+#pragma unroll
+            for (int e = 0; e < KQ / 4; ++e)
+                kv[e] = load4<Act>(kr + 4 * e);
+#pragma unroll
+            for (int e = 0; e < KQ / 4; ++e) {
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(xc + 4 * e);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    ss = __builtin_fmaf(kv[u], kv[u], ss);
-                    acc = __builtin_fmaf(kv[u], xv[u], acc);
+                    ss[u] = __builtin_fmaf(kv[e][u], kv[e][u], ss[u]);
+                    acc[u] = __builtin_fmaf(kv[e][u], xv[u], acc[u]);
                 }
             }
-            acc *= 1.0f / sqrtf(ss + p.eps);
         } else {
-            const float* xr = Xs + (j - hist) * p.KX;
-#pragma unroll 4
-            for (int e = 0; e < K; e += 4) {
-                const f32x4 kv = *reinterpret_cast<const f32x4*>(xr + e);
-                const f32x4 xv = *reinterpret_cast<const f32x4*>(Xs + c * p.KX + e);
+            const float* xr = Xs + (j - hist) * p.KX + sub * KQ;
+#pragma unroll
+            for (int e = 0; e < KQ / 4; ++e) {
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(xr + 4 * e);
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(xc + 4 * e);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    acc = __builtin_fmaf(kv[u], xv[u], acc);
+                    acc[u] = __builtin_fmaf(kv[u], xv[u], acc[u]);
             }
         }
-        P[j * PC + c] = acc;
+        float a4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        float s4 = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+        a4 += dpp<0xB1>(a4);          // quad_perm [1,0,3,2]
+        a4 += dpp<0x4E>(a4);          // quad_perm [2,3,0,1]
+        s4 += dpp<0xB1>(s4);
+        s4 += dpp<0x4E>(s4);
+        if (sub == 0)
+            P[j * PC + c] = j < hist ? a4 * (1.0f / sqrtf(s4 + p.eps)) : a4;
     }
     // ---- 2c. S0 [kh_w, qh_w] for this wave's 16 rows, four columns per group
     if (has_rows) {
@@ -294,21 +330,35 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
     __syncthreads();
 
     // ---- 4. history through the stored deltas: each thread group takes
-    // every kDcGroups-th record for its value row
-    const int grp = tid / kDcRows, vr = tid % kDcRows;
-    float hA[kTMax], hF[kTMax];
+    // every kDcGroups-th record for its value row (the first kDPre from the
+    // registers loaded at the start)
+    float hA[TM], hF[TM];
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t) {
+    for (int t = 0; t < TM; ++t) {
         hA[t] = 0.0f;
         hF[t] = 0.0f;
     }
     if (vr < BV) {
-        const float* dring = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v0 + vr;
-        for (int j = grp; j < hist; j += kDcGroups) {
+#pragma unroll
+        for (int m = 0; m < kDPre; ++m) {
+            const int j = grp + kDcGroups * m;
+            if (j < hist) {                      // wave-uniform
+                const float dj = dpre[m];
+                const float* cj = P + j * PC;
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    if (t < T) {
+                        hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
+                        hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
+                    }
+                }
+            }
+        }
+        for (int j = grp + kDcGroups * kDPre; j < hist; j += kDcGroups) {
             const float dj = dring[static_cast<size_t>((base + j) & (L - 1)) * V];
             const float* cj = P + j * PC;
 #pragma unroll
-            for (int t = 0; t < kTMax; ++t) {
+            for (int t = 0; t < TM; ++t) {
                 if (t < T) {
                     hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
                     hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
@@ -318,7 +368,7 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
         if (grp > 0) {
             float* pr = part + ((grp - 1) * kDcRows + vr) * 2 * kTMax;
 #pragma unroll
-            for (int t = 0; t < kTMax; ++t) {
+            for (int t = 0; t < TM; ++t) {
                 if (t < T) {
                     pr[t] = hA[t];
                     pr[kTMax + t] = hF[t];
@@ -337,7 +387,7 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
             for (int gq = 1; gq < kDcGroups; ++gq) {
                 const float* pr = part + ((gq - 1) * kDcRows + vr) * 2 * kTMax;
 #pragma unroll
-                for (int t = 0; t < kTMax; ++t) {
+                for (int t = 0; t < TM; ++t) {
                     if (t < T) {
                         hA[t] += pr[t];
                         hF[t] += pr[kTMax + t];
@@ -345,13 +395,13 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
                 }
             }
             const int v = v0 + vr;
-            float dw[kTMax];
+            float dw[TM];
             const float* spr = SP + vr * PC;
             using st = typename Act::storage;
             st* out = static_cast<st*>(p.o);
-            float* dring = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v;
+            float* dout = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v;
 #pragma unroll
-            for (int i = 0; i < kTMax; ++i) {
+            for (int i = 0; i < TM; ++i) {
                 dw[i] = 0.0f;
                 if (i < T) {
                     const int ii = hist + i;
@@ -359,21 +409,21 @@ __global__ __launch_bounds__(kDcThreads, 2) void dcache_verify_kernel(const DcPa
                     const float vi = act_at<Act>(p.v, (tok * HV + hv) * V + v);
                     float d = bet[ii] * (vi - exp2f(gam[ii]) * spr[i]) - hA[i];
 #pragma unroll
-                    for (int i2 = 0; i2 < kTMax; ++i2)
+                    for (int i2 = 0; i2 < TM; ++i2)
                         if (i2 < i)
                             d = __builtin_fmaf(-P[(hist + i2) * PC + i], dw[i2], d);
                     dw[i] = d;
                     if (p.write_ring)
-                        dring[static_cast<size_t>((wp_phys0 + i) & (L - 1)) * V] = d;
+                        dout[static_cast<size_t>((wp_phys0 + i) & (L - 1)) * V] = d;
                 }
             }
 #pragma unroll
-            for (int t = 0; t < kTMax; ++t) {
+            for (int t = 0; t < TM; ++t) {
                 if (t < T) {
                     const int it = hist + t;
                     float acc = exp2f(gam[it]) * spr[TP + t] + hF[t];
 #pragma unroll
-                    for (int i = 0; i < kTMax; ++i)
+                    for (int i = 0; i < TM; ++i)
                         if (i <= t)
                             acc = __builtin_fmaf(P[(hist + i) * PC + TP + t], dw[i], acc);
                     const size_t tok = static_cast<size_t>(b) * T + t;
@@ -434,10 +484,10 @@ size_t dcache_lds_bytes(const gdn_shape& sh)
     return f * 4;
 }
 
-template <class Act, int K>
+template <class Act, int K, int TM>
 static hipError_t launch_dc_k(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
 {
-    auto kern = dcache_verify_kernel<Act, K>;
+    auto kern = dcache_verify_kernel<Act, K, TM>;
     const size_t lds = dcache_lds_bytes(sh);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -451,13 +501,23 @@ static hipError_t launch_dc_k(const gdn_shape& sh, const DcParams& p, hipStream_
     return hipGetLastError();
 }
 
+template <class Act, int K>
+static hipError_t launch_dc_t(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
+{
+    if (sh.T <= 4)
+        return launch_dc_k<Act, K, 4>(sh, p, stream);
+    if (sh.T <= 8)
+        return launch_dc_k<Act, K, 8>(sh, p, stream);
+    return launch_dc_k<Act, K, kTMax>(sh, p, stream);
+}
+
 template <class Act>
 static hipError_t launch_dc_act(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
 {
     switch (sh.K) {
-    case 64: return launch_dc_k<Act, 64>(sh, p, stream);
-    case 128: return launch_dc_k<Act, 128>(sh, p, stream);
-    case 256: return launch_dc_k<Act, 256>(sh, p, stream);
+    case 64: return launch_dc_t<Act, 64>(sh, p, stream);
+    case 128: return launch_dc_t<Act, 128>(sh, p, stream);
+    case 256: return launch_dc_t<Act, 256>(sh, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
