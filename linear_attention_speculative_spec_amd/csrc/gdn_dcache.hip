@@ -137,7 +137,56 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     const int v0 = vt * kDcRows;
     const int BV = (V - v0) < kDcRows ? (V - v0) : kDcRows;
 
-    // ---- 1. checkpoint rows of this wave (in flight while the rest stages)
+    // ---- 1. Loads, small ones first: the waits for the gate inputs, window
+    // values and window columns then never wait on the checkpoint stream
+    // behind them (vector-memory waits count loads in issue order).
+    const int grp = tid / kDcRows, vr = tid % kDcRows;   // (wave-uniform grp)
+    // gate inputs of the combined sequence (record j = tid < n): history from
+    // the ring, window a and b
+    float gin_a = 0.0f, gin_b = 0.0f;
+    const size_t gbase = (static_cast<size_t>(s) * HV + hv) * L;
+    const bool gate_thread = tid < n;
+    if (gate_thread) {
+        if (tid < hist) {
+            const int ph = (base + tid) & (L - 1);
+            gin_a = p.rg[gbase + ph];
+            gin_b = p.rb[gbase + ph];
+        } else {
+            const size_t tok = static_cast<size_t>(b) * T + (tid - hist);
+            gin_a = act_at<Act>(p.a, tok * HV + hv);
+            gin_b = act_at<Act>(p.b, tok * HV + hv);
+        }
+    }
+    // the window values of this thread's value row (used in step 5 by group 0)
+    float vwin[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        vwin[i] = 0.0f;
+    if (grp == 0 && vr < BV) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int ic = i < T ? i : T - 1;
+            const size_t tok = static_cast<size_t>(b) * T + ic;
+            vwin[i] = act_at<Act>(p.v, (tok * HV + hv) * V + v0 + vr);
+        }
+    }
+    // the first window column of this wave (window keys are columns 0..TP-1,
+    // queries TP..2TP-1; zero past T)
+    auto column_loads = [&](int c, float (&x)[K / 64]) {
+        const bool isq = c >= TP;
+        const int t = isq ? c - TP : c;
+#pragma unroll
+        for (int e = 0; e < K / 64; ++e) {
+            x[e] = 0.0f;
+            if (t < T) {
+                const size_t tok = static_cast<size_t>(b) * T + t;
+                x[e] = act_at<Act>(isq ? p.q : p.k, (tok * H + h) * K + 64 * e + lane);
+            }
+        }
+    };
+    float x0[K / 64];
+    column_loads(wave < PC ? wave : 0, x0);
+    // checkpoint rows of this wave (in flight while the rest stages)
     const bool has_rows = wave * 16 < BV;
     const int r0 = v0 + (has_rows ? wave * 16 : 0);
     const float* Srow = p.S + ((static_cast<size_t>(s) * HV + hv) * V + r0 + (lane & 7)) * K + 4 * (lane >> 3);
@@ -146,10 +195,8 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     for (int i = 0; i < K / 16; ++i)
         sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + (i & 1) * 8 * K + (i >> 1) * 32));
     // the stored deltas this thread sums in step 4 (records grp + kDcGroups m,
-    // the first kDPre of them), issued now so their latency hides behind the
-    // staging; indices past the history are clamped to a valid record and
-    // skipped in step 4
-    const int grp = tid / kDcRows, vr = tid % kDcRows;   // (wave-uniform grp)
+    // the first kDPre of them); indices past the history are clamped to a
+    // valid record and skipped in step 4
     const float* dring = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v0 + vr;
     float dpre[kDPre];
 #pragma unroll
@@ -164,40 +211,34 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
         }
     }
 
-    // window keys (columns 0..TP-1) and queries (TP..2TP-1), normalised; one
-    // wave per column, zero columns past T
+    // window columns normalised into LDS, one wave per column
     for (int c = wave; c < PC; c += kDcWaves) {
         const bool isq = c >= TP;
         const int t = isq ? c - TP : c;
         float x[K / 64];
+        if (c == wave) {
+#pragma unroll
+            for (int e = 0; e < K / 64; ++e)
+                x[e] = x0[e];
+        } else {
+            column_loads(c, x);
+        }
         float ss = 0.0f;
 #pragma unroll
-        for (int e = 0; e < K / 64; ++e) {
-            x[e] = 0.0f;
-            if (t < T) {
-                const size_t tok = static_cast<size_t>(b) * T + t;
-                x[e] = act_at<Act>(isq ? p.q : p.k, (tok * H + h) * K + 64 * e + lane);
-            }
+        for (int e = 0; e < K / 64; ++e)
             ss = __builtin_fmaf(x[e], x[e], ss);
-        }
         ss = group_sum<64>(ss);
         const float rn = t < T ? 1.0f / sqrtf(ss + p.eps) : 0.0f;
 #pragma unroll
         for (int e = 0; e < K / 64; ++e)
             Xs[c * p.KX + 64 * e + lane] = x[e] * rn;
     }
-    // gates of the combined sequence: history from the ring, window computed
-    const size_t gbase = (static_cast<size_t>(s) * HV + hv) * L;
-    for (int j = tid; j < n; j += kDcThreads) {
-        float g, be;
-        if (j < hist) {
-            const int ph = (base + j) & (L - 1);
-            g = p.rg[gbase + ph];
-            be = p.rb[gbase + ph];
-        } else {
-            const size_t tok = static_cast<size_t>(b) * T + (j - hist);
-            gdn_gate(act_at<Act>(p.a, tok * HV + hv), act_at<Act>(p.b, tok * HV + hv), p.A_log[hv],
-                     p.dt_bias[hv], p.softplus_threshold, g, be);
+    // gates of the combined sequence: history as recorded, window computed
+    if (gate_thread) {
+        const int j = tid;
+        float g = gin_a, be = gin_b;
+        if (j >= hist) {
+            gdn_gate(gin_a, gin_b, p.A_log[hv], p.dt_bias[hv], p.softplus_threshold, g, be);
             wg[j - hist] = g;
             wg[kTMax + j - hist] = be;
         }
@@ -405,9 +446,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
                 dw[i] = 0.0f;
                 if (i < T) {
                     const int ii = hist + i;
-                    const size_t tok = static_cast<size_t>(b) * T + i;
-                    const float vi = act_at<Act>(p.v, (tok * HV + hv) * V + v);
-                    float d = bet[ii] * (vi - exp2f(gam[ii]) * spr[i]) - hA[i];
+                    float d = bet[ii] * (vwin[i] - exp2f(gam[ii]) * spr[i]) - hA[i];
 #pragma unroll
                     for (int i2 = 0; i2 < TM; ++i2)
                         if (i2 < i)
