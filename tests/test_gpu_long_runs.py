@@ -201,10 +201,15 @@ def test_fold_every_commit_matches_ring_with_history():
 
 # ------------------------------------------------- long-window drift, T=8 L=128
 
-def drift_run(variant: str, iters: int, seed: int, n_orows: int = 4, check_every: int = 32):
+def drift_run(variant: str, iters: int, seed: int, n_orows: int = 4, check_every: int = 32,
+              dcache: bool = False):
+    """With ``dcache`` the GPU verifies through its ring of stored deltas while
+    the oracle keeps replaying the raw records: any drift of the stored fp32
+    deltas shows in the outputs."""
     shape = synth.CONFIGS["long_window_t8"]
     pick = np.sort(synth.make_rng(seed + 1).choice(shape.B, n_orows, replace=False))
-    P = Pair(shape, seed, variant, oracle_rows=pick)
+    P = Pair(shape, seed, variant, oracle_rows=pick, dcache=dcache)
+    gpu_verify = P.gpu.verify_dcache if dcache else P.gpu.verify
     dw = synth.DeviceWindows(seed + 2, shape, variant)
     accepts = synth.accept_counts(P.rng, shape.B, shape.T, iters)
     tol = TOL[shape.act]
@@ -217,7 +222,7 @@ def drift_run(variant: str, iters: int, seed: int, n_orows: int = 4, check_every
         win = dw.draw()
         o = P.gpu.new_out()
         flagged = P.ocur.is_flush[P.oslots].astype(bool)
-        P.gpu.verify(P.dcur, P.dslots, _DevWin(win), o)          # folds flagged rows
+        gpu_verify(P.dcur, P.dslots, _DevWin(win), o)            # folds flagged rows
         w64 = helpers.win_f64(dw.host_rows(win, P.orows, shape.T), shape.act)
         if i % check_every == 0 or i == iters - 1:
             ref = P.orc.verify(P.ocur, P.oslots, w64)
@@ -242,7 +247,7 @@ def drift_run(variant: str, iters: int, seed: int, n_orows: int = 4, check_every
         if i % 64 == 0 or i == iters - 1:
             _cursors_equal(P.dcur, P.cur, i)
         if i % 512 == 511:
-            say(f"drift {variant}: {i + 1}/{iters} iterations, {int(nflush.sum())} oracle-row "
+            say(f"drift {variant}{' d-cache' if dcache else ''}: {i + 1}/{iters} iterations, {int(nflush.sum())} oracle-row "
                 f"flushes, {time.time() - t0:.0f}s")
     return s_curve, o_curve
 
@@ -251,10 +256,12 @@ def _drift_iters() -> int:
     return int(os.environ.get("GDN_DRIFT_ITERS", "4096"))
 
 
-@pytest.mark.parametrize("variant", ["base", "low_decay"])
+@pytest.mark.parametrize("variant", ["base", "low_decay", "low_decay_dcache"])
 def test_long_window_drift_curve(variant):
     iters = _drift_iters()
-    s_curve, o_curve = drift_run(variant, iters, 1003 if variant == "base" else 1013)
+    dcache = variant.endswith("_dcache")
+    law = variant[:-len("_dcache")] if dcache else variant
+    s_curve, o_curve = drift_run(law, iters, 1003 if law == "base" else 1013, dcache=dcache)
     # the curve: worst checkpoint error per flush number over the followed rows
     by_flush = {}
     for _, _, n, e in s_curve:
