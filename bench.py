@@ -264,6 +264,7 @@ def main():
     log(f"[bench] step {ms_step * 1e3:.1f} us, verify {v_avg_us:.1f} us "
         f"({achieved:.0f} GB/s), fold {fold_ms.mean() * 1e3:.1f} us")
 
+    traffic = traffic_from_profile()
     result = {
         "metric": "GDN verify draft tokens/s per layer",
         "value": tokens / (ms_step * 1e-3),
@@ -288,7 +289,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_from_profile(),
+            "traffic": traffic,
+            "traffic_GBs": (traffic / (v_avg_us * 1e-6) / 1e9) if traffic else None,
             "alg_bytes_per_launch": float(vbytes.mean()),
             "avg_launch_us": v_avg_us,
         },
