@@ -14,6 +14,8 @@
 // recurrence kernels run the identical per-record arithmetic (rnorm16,
 // step_row from gdn_common.h), which is what makes the fold of a recorded
 // window bit-identical to the snapshot of the same window.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -95,25 +97,36 @@ __device__ __forceinline__ void store_cols_f32(float* row, int c, const float (&
 
 // Records of the fold are staged through LDS in batches of kFoldBatch,
 // double-buffered: the loads of batch i+1 are in flight while the sequential
-// steps of batch i run from LDS.
+// steps of batch i run from LDS.  Each thread loads the raw key columns it
+// normalises itself (record tid / 16 of the batch, columns 64 m + 4 c .. +3),
+// so raw keys never pass through LDS.
 constexpr int kFoldBatch = 16;
 
 template <class Act, int K>
 struct FoldStage {
-    static constexpr int KU = K * Act::bytes / 16;            // 16-byte units per key
     static constexpr int VU = 16 * Act::bytes / 16;           // units of 16 values
-    static constexpr int KUB = kFoldBatch * KU;               // key units per batch
     static constexpr int VUB = kFoldBatch * VU;
-    static constexpr int KPT = (KUB + 255) / 256;             // key units per thread
+    typedef typename std::conditional<Act::bytes == 4, uint4, uint2>::type KRaw;   // 4 activations
 };
 
 template <class Act, int K>
 struct FoldShared {
-    uint4 kbuf[2][FoldStage<Act, K>::KUB];          // raw keys of a batch
     uint4 vbuf[2][FoldStage<Act, K>::VUB];          // this tile's 16 values per record
-    float gbuf[2][kFoldBatch], bbuf[2][kFoldBatch];  // gate (then decay) and beta
+    float gbuf[2][kFoldBatch], bbuf[2][kFoldBatch];  // decay e^g and beta
     float khs[2][kFoldBatch][K];                     // normalised keys
 };
+
+// Four raw activations widened to fp32 exactly as load4 widens them.
+__device__ __forceinline__ f32x4 widen4(uint4 u)
+{
+    return f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+}
+
+__device__ __forceinline__ f32x4 widen4(uint2 u)
+{
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+}
 
 // Fold of one work item: the n committed records of slot s into 16 rows
 // (tile) of one layer's value head hv.  Called uniformly by the workgroup.
@@ -123,9 +136,9 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
 {
     using st = typename Act::storage;
     using FS = FoldStage<Act, K>;
+    using KRaw = typename FS::KRaw;
     constexpr int EPL = K / 16;
     constexpr int RB = kFoldBatch;
-    auto& kbuf = sh.kbuf;
     auto& vbuf = sh.vbuf;
     auto& gbuf = sh.gbuf;
     auto& bbuf = sh.bbuf;
@@ -151,18 +164,17 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
     const float* rb = p.rb + gofs;
 
     // registers of one batch in flight
-    uint4 kreg[FS::KPT];
+    KRaw kreg[K / 64];
     uint4 vreg;
     float greg;
     auto issue = [&](int bi) {
+        const int jk = bi * RB + row16;
 #pragma unroll
-        for (int i = 0; i < FS::KPT; ++i) {
-            const int u = i * 256 + tid;
-            const int j = bi * RB + u / FS::KU;
-            kreg[i] = uint4{0u, 0u, 0u, 0u};
-            if (u < FS::KUB && j < n) {
-                const int ph = (base + j) & (L - 1);
-                kreg[i] = reinterpret_cast<const uint4*>(rk + static_cast<size_t>(ph) * K)[u % FS::KU];
+        for (int m = 0; m < K / 64; ++m) {
+            kreg[m] = KRaw{};
+            if (jk < n) {
+                const int ph = (base + jk) & (L - 1);
+                kreg[m] = *reinterpret_cast<const KRaw*>(rk + static_cast<size_t>(ph) * K + 64 * m + 4 * c);
             }
         }
         vreg = uint4{0u, 0u, 0u, 0u};
@@ -183,34 +195,32 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
         }
     };
     auto commit = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < FS::KPT; ++i) {
-            const int u = i * 256 + tid;
-            if (u < FS::KUB)
-                kbuf[buf][u] = kreg[i];
-        }
         if (tid < FS::VUB) {
             vbuf[buf][tid] = vreg;
         } else if (tid >= 128 && tid < 128 + 2 * RB) {
             const int r = tid - 128;
             if (r < RB)
-                gbuf[buf][r] = greg;
+                gbuf[buf][r] = expf(greg);
             else
                 bbuf[buf][r - RB] = greg;
         }
     };
 
-    // 16 lane groups normalise the 16 keys of a batch in parallel
+    // 16 lane groups normalise the 16 keys of a batch in parallel, from the
+    // registers their own loads filled
     auto prep = [&](int buf, int cnt) {
         const int jj = row16;
+        float kc[EPL], kh[EPL];
+#pragma unroll
+        for (int m = 0; m < K / 64; ++m) {
+            const f32x4 t = widen4(kreg[m]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                kc[4 * m + e] = t[e];
+        }
         if (jj < cnt) {
-            float kc[EPL], kh[EPL];
-            const st* kb = reinterpret_cast<const st*>(kbuf[buf]);
-            load_cols<Act, K>(kb + jj * K, c, kc);
             prep_key<EPL>(kc, p.eps, kh);
             store_cols_f32<K>(sh.khs[buf][jj], c, kh);
-            if (c == 0)
-                gbuf[buf][jj] = expf(gbuf[buf][jj]);
         }
     };
 
@@ -218,7 +228,6 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
     float sv[EPL];
     load_cols_f32<K>(Srow, c, sv);
     commit(0);
-    __syncthreads();
     prep(0, min(RB, n));
     __syncthreads();
 
@@ -234,9 +243,10 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
             load_cols_f32<K>(sh.khs[buf][jj], c, kh);
             step_row<EPL>(sv, kh, Act::load(vb + jj * 16 + row16), gbuf[buf][jj], bbuf[buf][jj]);
         }
+        // buffer buf ^ 1 was last read by the previous batch's steps, which
+        // every thread finished before the barrier that ended that batch
         if (bi + 1 < nbatch) {
             commit(buf ^ 1);
-            __syncthreads();
             prep(buf ^ 1, min(RB, n - (bi + 1) * RB));
         }
         __syncthreads();
@@ -248,7 +258,7 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
 // Persistent fold: every workgroup compacts the rows to fold (in chunks of
 // kFoldRows) into LDS, then strides over the work items (row, layer, value
 // head, 16-row tile).  Rows with nothing to fold cost no workgroup.
-constexpr int kFoldRows = 1024;
+constexpr int kFoldRows = 512;
 
 template <class Act, int K>
 __global__ __launch_bounds__(256) void fold_kernel(const RecParams p, int num_layers)
@@ -455,7 +465,10 @@ template <class Act>
 static hipError_t launch_fold_act(const gdn_shape& sh, int num_layers, const RecParams& p,
                                   hipStream_t stream)
 {
-    // persistent grid: enough workgroups to fill the chip, never more than items
+    // persistent grid of 2048 workgroups, never more than items.  That is more
+    // than fit at once (7 per compute unit at K = 128): the ones that wait for
+    // a slot balance the load.  A grid of exactly the resident workgroups
+    // was slower both for a few flagged rows and for folding every row.
     const long long items = static_cast<long long>(sh.B) * num_layers * sh.HV * (sh.V / 16);
     const unsigned grid = static_cast<unsigned>(items < 2048 ? items : 2048);
     switch (sh.K) {
