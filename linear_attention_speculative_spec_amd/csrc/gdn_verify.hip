@@ -105,21 +105,19 @@ struct VCfg {
     static constexpr int KP = K + 8;               // LDS X row, bf16 elements (16-byte pad)
     static constexpr int NXR = LM + 16;            // X rows: keys (< LM), 16 query rows at NQ0
     static constexpr int VP = BVM + EPC;           // LDS value row, activations (16-byte pad)
-    // F / U row stride (floats; U is zero past n).  24 mod 64 banks: the
-    // value part's reads of four U rows at eight records each hit 32
-    // distinct banks.
-    static constexpr int FST = LM + 24;
+    static constexpr int FST = LM + 20;            // F / U row stride (floats; U is zero past n)
     static constexpr int CST = LM + 20;            // Z coefficient row stride (floats)
     static constexpr int NBM = LM / 16;            // 16-row key blocks
     // A is stored per 16-row block I as a dense panel of 16 rows x 16 (I + 1)
     // columns (row stride 16 I + 20): only the part at or left of the block
     // diagonal exists.
     static constexpr int A_FLOATS = 128 * NBM * (NBM + 1) + 64 * NBM;
-    // Z row stride (floats).  32 mod 64 banks where A's space allows: the
-    // output products read four Z rows at eight 16-byte column groups, and
-    // rows 0, 2 and rows 1, 3 then fall on disjoint halves of the banks
-    // (two passes, the least for 512 bytes).
-    static constexpr int ZST = 16 * (K + 32) <= A_FLOATS ? K + 32 : K + 4;
+    // Z row stride (floats), where A's space allows it.  The output products
+    // read four Z rows at eight 16-byte column groups per instruction; of the
+    // strides K + 4, K + 16 and K + 32, K + 16 gives the fewest LDS
+    // bank-conflict cycles (SQ_LDS_BANK_CONFLICT 5.2 M, 2.1 M and 3.1 M per
+    // launch at B=256, K=V=128, T=4).
+    static constexpr int ZST = 16 * (K + 16) <= A_FLOATS ? K + 16 : K + 4;
     static constexpr int Z_FLOATS = 16 * ZST;     // up to 16 window columns
     static constexpr int AZ = A_FLOATS > Z_FLOATS ? A_FLOATS : Z_FLOATS;
     static constexpr int VCRM = BVM / EPC;         // chunks per value row at most
