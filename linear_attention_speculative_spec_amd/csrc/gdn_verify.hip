@@ -102,7 +102,11 @@ struct VCfg {
     static constexpr int EPC = 16 / eb;            // activations per 16-byte chunk
     static constexpr int CPR = K / EPC;            // chunks per key row
     static constexpr int CSH = ilog2c(CPR);
-    static constexpr int KP = K + 8;               // LDS X row, bf16 elements (16-byte pad)
+    // LDS X row, bf16 elements.  A 32-byte pad: with 16 bytes the Gram tiles'
+    // 16-byte operand reads and the staging writes conflicted on the banks
+    // (SQ_LDS_BANK_CONFLICT 1.9 M cycles per launch at B=256, K=V=128, T=4);
+    // with 32 they read zero.
+    static constexpr int KP = K + 16;
     static constexpr int NXR = LM + 16;            // X rows: keys (< LM), 16 query rows at NQ0
     static constexpr int VP = BVM + EPC;           // LDS value row, activations (16-byte pad)
     static constexpr int FST = LM + 20;            // F / U row stride (floats; U is zero past n)
