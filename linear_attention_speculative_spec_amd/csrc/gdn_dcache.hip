@@ -47,6 +47,11 @@ constexpr int kDcWaves = 8;
 constexpr int kDcThreads = 64 * kDcWaves;
 constexpr int kDcRows = 128;          // value rows per workgroup (16 per wave)
 constexpr int kDcGroups = kDcThreads / kDcRows;   // thread groups over the history
+// LDS arrays indexed by value row are stored column by column, so that the
+// lanes of a wave (consecutive value rows) touch consecutive banks.  The
+// column stride of SP is padded by 16 floats: its writes put four columns of
+// 16 rows in one instruction, on disjoint banks.
+constexpr int kSPS = kDcRows + 16;
 constexpr int kTMax = 16;             // window tokens at most (max_spec_len <= 16)
 constexpr int kDPre = 16;             // stored deltas per thread loaded at the start
 constexpr float kLog2eDc = 1.4426950408889634f;
@@ -116,8 +121,8 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     float* bet = sm + p.o_bet;     // [n] beta
     float* wg = sm + p.o_wg;       // [2 kTMax] window g then beta (for the ring)
     float* P = sm + p.o_p;         // [L][PC] dot products, then coefficients
-    float* SP = sm + p.o_sp;       // [kDcRows][PC] S0 times the window columns
-    float* part = sm + p.o_part;   // [kDcGroups - 1][kDcRows][2T] history partial sums
+    float* SP = sm + p.o_sp;       // [PC][kSPS] S0 times the window columns (column c, value row r)
+    float* part = sm + p.o_part;   // [kDcGroups - 1][2 kTMax][kDcRows] history partial sums
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int item = blockIdx.x;
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
                 val = c == r ? sl : (c == 4 + r ? sh : val);
             }
             const int row = wave * 16 + (lane & 7) + 8 * (c >> 2);
-            SP[row * PC + 4 * cg + (c & 3)] = val;
+            SP[(4 * cg + (c & 3)) * kSPS + row] = val;
         }
     }
     __syncthreads();
@@ -407,12 +412,12 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
             }
         }
         if (grp > 0) {
-            float* pr = part + ((grp - 1) * kDcRows + vr) * 2 * kTMax;
+            float* pr = part + (grp - 1) * 2 * kTMax * kDcRows + vr;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 if (t < T) {
-                    pr[t] = hA[t];
-                    pr[kTMax + t] = hF[t];
+                    pr[t * kDcRows] = hA[t];
+                    pr[(kTMax + t) * kDcRows] = hF[t];
                 }
             }
         }
@@ -426,18 +431,18 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
         if (vr < BV) {
 #pragma unroll
             for (int gq = 1; gq < kDcGroups; ++gq) {
-                const float* pr = part + ((gq - 1) * kDcRows + vr) * 2 * kTMax;
+                const float* pr = part + (gq - 1) * 2 * kTMax * kDcRows + vr;
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     if (t < T) {
-                        hA[t] += pr[t];
-                        hF[t] += pr[kTMax + t];
+                        hA[t] += pr[t * kDcRows];
+                        hF[t] += pr[(kTMax + t) * kDcRows];
                     }
                 }
             }
             const int v = v0 + vr;
             float dw[TM];
-            const float* spr = SP + vr * PC;
+            const float* spr = SP + vr;
             using st = typename Act::storage;
             st* out = static_cast<st*>(p.o);
             float* dout = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v;
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
                 dw[i] = 0.0f;
                 if (i < T) {
                     const int ii = hist + i;
-                    float d = bet[ii] * (vwin[i] - exp2f(gam[ii]) * spr[i]) - hA[i];
+                    float d = bet[ii] * (vwin[i] - exp2f(gam[ii]) * spr[i * kSPS]) - hA[i];
 #pragma unroll
                     for (int i2 = 0; i2 < TM; ++i2)
                         if (i2 < i)
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
             for (int t = 0; t < TM; ++t) {
                 if (t < T) {
                     const int it = hist + t;
-                    float acc = exp2f(gam[it]) * spr[TP + t] + hF[t];
+                    float acc = exp2f(gam[it]) * spr[(TP + t) * kSPS] + hF[t];
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
                         if (i <= t)
@@ -512,13 +517,13 @@ size_t dcache_lds_bytes(const gdn_shape& sh)
 {
     const int TP = (sh.T + 3) & ~3;
     const int PC = 2 * TP;
-    const int KX = sh.K + 4;
+    const int KX = sh.K + 16;
     size_t f = 0;
     f += static_cast<size_t>(PC) * KX;               // Xs
     f += 2 * static_cast<size_t>(sh.L);              // gam, bet
     f += 2 * kTMax;                                  // wg
     f += static_cast<size_t>(sh.L) * PC;             // P
-    f += static_cast<size_t>(kDcRows) * PC;          // SP
+    f += static_cast<size_t>(PC) * kSPS;             // SP
     f += static_cast<size_t>(kDcGroups - 1) * kDcRows * 2 * kTMax;   // part
     return f * 4;
 }
@@ -600,14 +605,14 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
     p.rd = ring_d;
     p.o = o;
     p.PC = 2 * p.TP;
-    p.KX = sh.K + 4;
+    p.KX = sh.K + 16;   // rows read four at a time as 16-byte groups: a 64-byte pad keeps them off each other's banks
     p.o_x = 0;
     p.o_gam = p.o_x + p.PC * p.KX;
     p.o_bet = p.o_gam + sh.L;
     p.o_wg = p.o_bet + sh.L;
     p.o_p = p.o_wg + 2 * kTMax;
     p.o_sp = p.o_p + sh.L * p.PC;
-    p.o_part = p.o_sp + kDcRows * p.PC;
+    p.o_part = p.o_sp + p.PC * kSPS;
     return sh.act == GDN_BF16 ? launch_dc_act<ActBF16>(sh, p, stream)
                               : launch_dc_act<ActF32>(sh, p, stream);
 }
