@@ -117,6 +117,13 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
 {
     extern __shared__ __align__(16) float sm[];
     float* Xs = sm + p.o_x;        // [PC][KX] normalised window keys, then queries
+    // Element k of a window column sits at xs_col(k): each quarter of the key
+    // (K / 4 elements, the share of one lane of a dot-product quad) is
+    // followed by 4 unused floats, so the quad's reads fall on distinct banks
+    // while each lane still reads (and loads) a contiguous quarter.  A row is
+    // K + 16 floats.
+    constexpr int KQ = K / 4;
+    auto xs_col = [](int k) { return k + 4 * (k / KQ); };
     float* gam = sm + p.o_gam;     // [n] log2(e) * prefix sums of g (raw g until the scan)
     float* bet = sm + p.o_bet;     // [n] beta
     float* wg = sm + p.o_wg;       // [2 kTMax] window g then beta (for the ring)
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
         const float rn = t < T ? 1.0f / sqrtf(ss + p.eps) : 0.0f;
 #pragma unroll
         for (int e = 0; e < K / 64; ++e)
-            Xs[c * p.KX + 64 * e + lane] = x[e] * rn;
+            Xs[c * p.KX + xs_col(64 * e + lane)] = x[e] * rn;
     }
     // gates of the combined sequence: history as recorded, window computed
     if (gate_thread) {
@@ -276,11 +283,10 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     // the normalised columns themselves).  Four lanes share a product, each
     // over a quarter of the key with all its loads issued first, and meet by
     // quad swaps.
-    constexpr int KQ = K / 4;
     for (int t4 = tid; t4 < n * PC * 4; t4 += kDcThreads) {
         const int sub = t4 & 3, task = t4 >> 2;
         const int j = task / PC, c = task % PC;
-        const float* xc = Xs + c * p.KX + sub * KQ;
+        const float* xc = Xs + c * p.KX + xs_col(sub * KQ);
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (j < hist) {
             const int ph = (base + j) & (L - 1);
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
                 }
             }
         } else {
-            const float* xr = Xs + (j - hist) * p.KX + sub * KQ;
+            const float* xr = Xs + (j - hist) * p.KX + xs_col(sub * KQ);
 #pragma unroll
             for (int e = 0; e < KQ / 4; ++e) {
                 const f32x4 kv = *reinterpret_cast<const f32x4*>(xr + 4 * e);
@@ -322,11 +328,11 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     // ---- 2c. S0 [kh_w, qh_w] for this wave's 16 rows, four columns per group
     if (has_rows) {
         for (int cg = 0; cg < PC / 4; ++cg) {
-            const float* xrow = Xs + (4 * cg + (lane & 3)) * p.KX + 4 * (lane >> 3);
+            const float* xrow = Xs + (4 * cg + (lane & 3)) * p.KX;
             f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, b0 = a0, b1 = a0;
 #pragma unroll
             for (int i = 0; i < K / 16; ++i) {
-                const f32x4 za = *reinterpret_cast<const f32x4*>(xrow + 32 * (i >> 1));
+                const f32x4 za = *reinterpret_cast<const f32x4*>(xrow + xs_col(4 * (lane >> 3) + 32 * (i >> 1)));
                 if (i & 1) {
                     a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a1, 0, 0, 0);
                     b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b1, 0, 0, 0);
