@@ -10,8 +10,12 @@ the HIP path; the only thing both sides share is the seeded input generator.
 * ``closed_form.py``- the chunked closed form, used only to pin the recurrence.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed form vs recurrence, special cases, the pages' worked cursor examples,
-fold identity, causality, base-shift invariance).  None is "parity unpinned".
+to something other than itself: the verify by an independent closed-form
+solve, special cases and causality; the fold by step-by-step replay; the
+snapshot baseline by a hand-computed two-token window and by the pinned fold
+of each window prefix; the cursor advance by the walks printed on the pages
+and by invariants; the cursor reset by its behaviour at the prefill -> decode
+handoff.  A planted mistake in each of them fails one of those tests.
 """
 from __future__ import annotations
 

@@ -544,3 +544,114 @@ def test_fold_consumes_exactly_the_committed_records():
     untouched = [s for s in range(shape.num_slots) if s not in set(slots.tolist())]
     for s in untouched:
         assert np.array_equal(layer.S[s], S_before[s])
+
+
+# --------------------------------------------------------- snapshot baseline
+
+def test_snapshot_hand_computed_two_token_window():
+    # the per-token baseline on a window small enough to follow by hand
+    with open(os.path.join(GOLDEN, "snapshot_t2.json")) as f:
+        gold = json.load(f)
+    g = gold["shape"]
+    shape = synth.LayerShape(B=g["B"], T=g["T"], H=g["H"], HV=g["HV"], K=g["K"], V=g["V"],
+                             L=g["L"], max_spec=g["max_spec"], num_slots=g["num_slots"],
+                             act="f32", scale=g["scale"], l2norm_eps=g["l2norm_eps"])
+    S0 = np.array(gold["S0"], float)[None, None]
+    layer = oracle.OracleLayer(shape, gold["A_log"], gold["dt_bias"], S0)
+    toks = gold["tokens"]
+    q = np.array([t["q"] for t in toks], float)[:, None, :]
+    k = np.array([t["k"] for t in toks], float)[:, None, :]
+    v = np.array([t["v"] for t in toks], float)[:, None, :]
+    a = np.array([[t["a"]] for t in toks], float)
+    b = np.array([[t["b"]] for t in toks], float)
+    o, snap = layer.snapshot(np.array([0], np.int32), (q, k, v, a, b))
+    for t, tok in enumerate(toks):
+        np.testing.assert_allclose(snap[0, t, 0], np.array(tok["snap"], float), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(o[t, 0], np.array(tok["o"], float), rtol=0, atol=1e-14)
+    # the checkpoint itself is read, never written
+    np.testing.assert_array_equal(layer.S[0, 0], np.array(gold["S0"], float))
+
+
+def test_snapshot_states_are_folds_of_the_window_prefixes():
+    # snap[b, t] is the committed state after accepting t + 1 drafts: the
+    # pinned exact fold of the window's records 0..t, recorded at a wrapping
+    # base, reproduces it; the outputs are the pinned verify's with an empty
+    # history.  Rows, tokens and heads all differ, so a transposed or shifted
+    # snapshot index fails.
+    shape = _tiny_shape(scale=0.9)
+    rng = synth.make_rng(91)
+    p = synth.layer_params(rng, shape, "low_decay")
+    layer = oracle.OracleLayer(shape, p.A_log, p.dt_bias, p.S0)
+    slots = synth.slot_choice(rng, shape)
+    slots[1] = -1                                         # one padding row
+    win64 = helpers.win_f64(synth.window(rng, shape, "low_decay"), shape.act)
+    S_before = layer.S.copy()
+    o_snap, snap = layer.snapshot(slots, win64)
+    np.testing.assert_array_equal(layer.S, S_before)
+    o_ver = layer.verify(CursorState.zeros(shape.num_slots), slots, win64, write_ring=False,
+                         fold_flagged=False)
+    live = [r for r, s in enumerate(slots) if s >= 0]
+    for r in live:
+        rows = slice(r * shape.T, (r + 1) * shape.T)
+        assert helpers.max_rel(o_snap[rows], o_ver[rows]) < 1e-12
+    # the padding row's outputs and snapshots are left as they were (NaN)
+    assert np.isnan(o_snap[shape.T:2 * shape.T]).all() and np.isnan(snap[1]).all()
+    for t in range(shape.T):
+        fold_layer = oracle.OracleLayer(shape, p.A_log, p.dt_bias, p.S0)
+        cur = CursorState.zeros(shape.num_slots)
+        cur.cache_base[:] = shape.L - 2                   # records 0..t wrap past the ring end
+        fold_layer.write_ring(cur, slots, win64)
+        cur.write_pos[:] = t + 1
+        cur.is_flush[:] = 1
+        fold_layer.fold(cur, slots, only_flagged=True)
+        for r in live:
+            s = int(slots[r])
+            np.testing.assert_allclose(snap[r, t], fold_layer.S[s], rtol=0, atol=1e-13)
+            assert helpers.max_rel(snap[r, t], fold_layer.S[s]) < 1e-12
+
+
+# ------------------------------------------------------------- cursor reset
+
+def test_reset_hands_slots_to_decode_with_an_empty_history():
+    # replayssm(B)SpecDecode App. A.2: at the prefill -> decode handoff a slot
+    # starts over from its checkpoint.  Pinned by behaviour: after the reset
+    # a verify of the slot equals the pinned snapshot path (no history), its
+    # window lands at physical positions 0..T-1, the next advance starts from
+    # zero, other slots keep their cursors, and list entries outside
+    # [0, num_slots) are skipped.
+    shape = _tiny_shape()
+    wp = np.array([7, 3, 12, 0, 9], np.int32)
+    base = np.array([5, 14, 9, 2, 11], np.int32)
+    layer, cur, slots, _, win, _ = _prefilled_layer(shape, 101, wp, base)
+    cur.is_flush[:] = [0, 1, 0, 0, 1]
+    win64 = helpers.win_f64(win, shape.act)
+    targets = [int(slots[0]), int(slots[2])]
+    for init_flush in (0, 1):
+        c = cur.copy()
+        oracle.reset(c, targets + [-1, shape.num_slots, 10 ** 6], init_flush=init_flush)
+        for s in range(shape.num_slots):
+            if s in targets:
+                assert (c.write_pos[s], c.cache_base[s], c.is_flush[s]) == (0, 0, init_flush)
+            else:
+                assert (c.write_pos[s], c.cache_base[s], c.is_flush[s]) == \
+                    (cur.write_pos[s], cur.cache_base[s], cur.is_flush[s])
+        lay = oracle.OracleLayer(shape, layer.A_log, layer.dt_bias, layer.S)
+        for n in ("rawk", "rawv", "g", "beta"):
+            setattr(lay, n, getattr(layer, n).copy())
+        S_before = lay.S.copy()
+        o = lay.verify(c, slots, win64, write_ring=True, fold_flagged=True)
+        o_snap, _ = lay.snapshot(slots, win64)
+        q, k, v, a, b = win64
+        for row in (0, 2):
+            s = int(slots[row])
+            rows = slice(row * shape.T, (row + 1) * shape.T)
+            assert helpers.max_rel(o[rows], o_snap[rows]) < 1e-12
+            np.testing.assert_array_equal(lay.S[s], S_before[s])   # nothing was folded
+            for t in range(shape.T):
+                np.testing.assert_array_equal(lay.rawk[s, :, t], k[row * shape.T + t])
+                np.testing.assert_array_equal(lay.rawv[s, :, t], v[row * shape.T + t])
+        acc = np.arange(len(slots), dtype=np.int32) % (shape.T + 1)
+        advance(c, slots, acc, shape.L, shape.T, shape.max_spec)
+        for row in (0, 2):
+            s = int(slots[row])
+            assert (c.write_pos[s], c.cache_base[s]) == (acc[row], 0)
