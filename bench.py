@@ -208,7 +208,7 @@ def main():
         w = wins[i % n_pool]
         if ev is not None:
             ev[0].record()
-        gv.gdn_exact_fold(gs, 1, S, rawk, rawv, rg, rb, dslots, cur[0], cur[1], cur[2], 1)
+        gv.gdn_exact_fold(gs, 1, 0, 0, S, rawk, rawv, rg, rb, dslots, cur[0], cur[1], cur[2], 1)
         if ev is not None:
             ev[1].record()
         gv.gdn_spec_verify_ring(gs, *w, A_log, dt_bias, S, dslots, cur[0], cur[1], cur[2],
@@ -358,7 +358,7 @@ def main():
             if ev is not None:
                 ev[1].record()
             gv.gdn_advance_cursors(gsf, dslots, acc_d[i % n_steps], *curf)
-            gv.gdn_exact_fold(gsf, 1, Sf, rkf, rvf, rgf, rbf, dslots, *curf, 0)
+            gv.gdn_exact_fold(gsf, 1, 0, 0, Sf, rkf, rvf, rgf, rbf, dslots, *curf, 0)
             if ev is not None:
                 ev[2].record()
             gv.gdn_reset_cursors(gsf, dslots, sh.B, 0, *curf)
@@ -408,7 +408,7 @@ def main():
             w = wins[i % n_pool]
             if ev is not None:
                 ev[0].record()
-            gv.gdn_exact_fold(gs, 1, Sd, rkd, rvd, rgd, rbd, dslots, *curd, 1)
+            gv.gdn_exact_fold(gs, 1, 0, 0, Sd, rkd, rvd, rgd, rbd, dslots, *curd, 1)
             if ev is not None:
                 ev[1].record()
             gv.gdn_spec_verify_dcache(gs, *w, A_log, dt_bias, Sd, dslots, *curd, rkd, rvd, rgd,

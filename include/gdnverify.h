@@ -74,6 +74,20 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   V % 16 == 0, 16 <= V <= 256; 0 <= B <= 65535; num_slots >= 1;
  *   act in {GDN_F32, GDN_BF16}; l2norm_eps >= 0; finite scale and threshold.
  * Anything else returns GDN_EINVAL (malformed) or GDN_EUNSUPPORTED.
+ *
+ * Why the supported envelope is narrower than "K, V multiples of 16 up to
+ * 256, L up to 256":
+ *  - K: a state row is spread over 16 lanes holding K/16 columns each in
+ *    4-wide vectors, and the closed form's key blocks are whole 64-column
+ *    MFMA tiles, so K must be a multiple of 64; the kernels are instantiated
+ *    for the three head widths 64, 128 and 256.
+ *  - L: the verify solves history and window as one system inside a
+ *    workgroup's LDS: up to L + 16 key rows, L + 16 value rows and the
+ *    strictly lower panels of A.  At L = 256 that exceeds the 160 KB of LDS of
+ *    a compute unit for every K, and at K = 256 already for L = 128; those
+ *    shapes return GDN_EUNSUPPORTED instead of running a slower fallback.
+ *  - max_spec_len <= 16: the window's query rows and Z columns are one
+ *    16-row MFMA block.
  */
 typedef struct gdn_shape {
     int32_t B, T, H, HV, K, V;
@@ -112,6 +126,10 @@ typedef struct gdn_shape {
  * S is never written for unflagged rows; cursors are never written.
  * o must not alias any input.  The ring pointers are always required (the
  * history is read from them even when write_ring = 0).
+ * bf16 gate inputs: a and b are read as aligned 4-byte words holding two
+ * activations, so for act = GDN_BF16 they must be 4-byte aligned
+ * (GDN_EINVAL otherwise) and B*T*HV must be even (GDN_EUNSUPPORTED
+ * otherwise), so that no word reaches past the last element.
  */
 int gdn_spec_verify_ring(const gdn_shape *shape,
                          const void *q, const void *k, const void *v,
@@ -180,13 +198,23 @@ size_t gdn_dring_bytes(const gdn_shape *shape);
  * so folding a ring written by a verify reproduces the snapshot path's state
  * bit for bit.  Cursors are not modified: a row folded while unflagged must
  * have its cursors rebased (e.g. gdn_reset_cursors) before its next verify.
- * num_layers >= 1 folds that many layers in one launch; S and the four ring
- * arrays then hold the layers back to back ([num_layers, ...] of the
- * per-layer layouts); cursors are shared by all layers.  shape->T is the
- * draft window of the verifies that wrote the ring (for the write_pos clamp);
- * q/k/v/a/b are not read.
+ * num_layers >= 1 folds that many layers in one launch (out-of-forward work,
+ * so the layer axis is parallel: PR #33102 report, the all-layer commit
+ * fold).  Layer l's checkpoint starts at S + l * layer_stride_S (fp32
+ * elements) and its ring at l * layer_stride_ring SLOTS past each ring base:
+ * ring_rawk + l*layer_stride_ring*H*L*K, ring_rawv + l*layer_stride_ring*HV*L*V,
+ * ring_g / ring_beta + l*layer_stride_ring*HV*L elements.  One slot count
+ * describes all four ring arrays of a pool whose layers are laid out
+ * [layer][slot][...].  A stride of 0 means back to back (num_slots*HV*V*K,
+ * num_slots).  With num_layers > 1 a nonzero stride must not make layers
+ * overlap (layer_stride_S >= num_slots*HV*V*K, layer_stride_ring >=
+ * num_slots), layer_stride_S must be a multiple of 4 (16-byte aligned
+ * layers), and negative strides are rejected (GDN_EINVAL).  Cursors are
+ * shared by all layers.  shape->T is the draft window of the verifies that
+ * wrote the ring (for the write_pos clamp); q/k/v/a/b are not read.
  */
 int gdn_exact_fold(const gdn_shape *shape, int num_layers,
+                   int64_t layer_stride_S, int64_t layer_stride_ring,
                    float *S, const void *ring_rawk, const void *ring_rawv,
                    const float *ring_g, const float *ring_beta,
                    const int32_t *slot_idx, const int32_t *write_pos,
@@ -224,6 +252,10 @@ int gdn_reset_cursors(const gdn_shape *shape, const int32_t *slots, int32_t n,
  * write_ring = 1 additionally records the window in the ring exactly as the
  * ring verify does (same positions, same g/beta bits); the ring and cursor
  * pointers may be NULL when write_ring = 0.  snap must not alias S.
+ * There is no is_flush argument: the window's records land at
+ * (cache_base + write_pos + t) & (L-1) whether or not the slot is flagged
+ * (for a flagged slot that is the next history's start), and this path
+ * reads no history, so the flag would change nothing it computes.
  */
 int gdn_recurrent_verify_snapshot(const gdn_shape *shape,
                                   const void *q, const void *k, const void *v,

@@ -127,13 +127,21 @@ int gdn_spec_verify_ring(const gdn_shape* shape, const void* q, const void* k, c
         return GDN_EINVAL;
     if (o == q || o == k || o == v || o == S)
         return GDN_EINVAL;
+    // bf16 gate inputs are read as aligned words of two activations: the
+    // words must be aligned and the last one must not reach past the end
+    if (sh.act == GDN_BF16) {
+        if (!aligned(a, 4) || !aligned(b, 4))
+            return GDN_EINVAL;
+        if ((static_cast<long long>(sh.B) * sh.T * sh.HV) % 2 != 0)
+            return GDN_EUNSUPPORTED;
+    }
     hipStream_t strm = static_cast<hipStream_t>(stream);
     const WindowPtrs w = {q, k, v, a, b, A_log, dt_bias};
     const CursorPtrs c = {write_pos, cache_base, is_flush};
     const RingPtrs r = {ring_rawk, ring_rawv, ring_g, ring_beta};
     if (fold_flagged) {
         // launch 1: rows flagged for flush advance their checkpoint exactly
-        st = status_of(launch_fold(sh, 1, S, r, slot_idx, c, 1, strm));
+        st = status_of(launch_fold(sh, 1, 0, 0, S, r, slot_idx, c, 1, strm));
         if (st != GDN_OK)
             return st;
     }
@@ -170,7 +178,7 @@ int gdn_spec_verify_dcache(const gdn_shape* shape, const void* q, const void* k,
     const RingPtrs r = {ring_rawk, ring_rawv, ring_g, ring_beta};
     if (fold_flagged) {
         // launch 1: flagged rows advance their checkpoint exactly (raw records)
-        st = status_of(launch_fold(sh, 1, S, r, slot_idx, c, 1, strm));
+        st = status_of(launch_fold(sh, 1, 0, 0, S, r, slot_idx, c, 1, strm));
         if (st != GDN_OK)
             return st;
     }
@@ -187,7 +195,8 @@ size_t gdn_dring_bytes(const gdn_shape* shape)
     return static_cast<size_t>(s.num_slots) * s.HV * s.L * s.V * 4;
 }
 
-int gdn_exact_fold(const gdn_shape* shape, int num_layers, float* S, const void* ring_rawk,
+int gdn_exact_fold(const gdn_shape* shape, int num_layers, int64_t layer_stride_S,
+                   int64_t layer_stride_ring, float* S, const void* ring_rawk,
                    const void* ring_rawv, const float* ring_g, const float* ring_beta,
                    const int32_t* slot_idx, const int32_t* write_pos, const int32_t* cache_base,
                    const int32_t* is_flush, int only_flagged, void* stream)
@@ -198,6 +207,17 @@ int gdn_exact_fold(const gdn_shape* shape, int num_layers, float* S, const void*
     const gdn_shape& sh = *shape;
     if (num_layers < 1 || static_cast<long long>(num_layers) * sh.HV > 65535)
         return num_layers < 1 ? GDN_EINVAL : GDN_EUNSUPPORTED;
+    // per-layer strides: fp32 elements of S, slots of the ring arrays
+    const int64_t layer_S = static_cast<int64_t>(sh.num_slots) * sh.HV * sh.V * sh.K;
+    if (layer_stride_S < 0 || layer_stride_ring < 0)
+        return GDN_EINVAL;
+    if (layer_stride_S == 0)
+        layer_stride_S = layer_S;
+    if (layer_stride_ring == 0)
+        layer_stride_ring = sh.num_slots;
+    if (num_layers > 1 &&
+        (layer_stride_S < layer_S || layer_stride_ring < sh.num_slots || layer_stride_S % 4 != 0))
+        return GDN_EINVAL;
     if (!ok_ptr(S, 16) || !ok_ptr(ring_rawk, 16) || !ok_ptr(ring_rawv, 16) || !ok_ptr(ring_g, 4) ||
         !ok_ptr(ring_beta, 4) || !ok_ptr(slot_idx, 4) || !ok_ptr(write_pos, 4) ||
         !ok_ptr(cache_base, 4) || (only_flagged && !ok_ptr(is_flush, 4)))
@@ -205,8 +225,8 @@ int gdn_exact_fold(const gdn_shape* shape, int num_layers, float* S, const void*
     const RingPtrs r = {const_cast<void*>(ring_rawk), const_cast<void*>(ring_rawv),
                         const_cast<float*>(ring_g), const_cast<float*>(ring_beta)};
     const CursorPtrs c = {write_pos, cache_base, is_flush};
-    return status_of(launch_fold(sh, num_layers, S, r, slot_idx, c, only_flagged ? 1 : 0,
-                                 static_cast<hipStream_t>(stream)));
+    return status_of(launch_fold(sh, num_layers, layer_stride_S, layer_stride_ring, S, r, slot_idx,
+                                 c, only_flagged ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_advance_cursors(const gdn_shape* shape, const int32_t* slot_idx, const int32_t* accept,

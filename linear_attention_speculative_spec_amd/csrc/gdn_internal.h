@@ -49,7 +49,10 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
                                 const int32_t* slot_idx, const CursorPtrs& c, const RingPtrs& r,
                                 float* ring_d, int write_ring, void* o, hipStream_t stream);
 
-hipError_t launch_fold(const gdn_shape& sh, int num_layers, float* S, const RingPtrs& r,
+// Layer l of a multi-layer fold: S + l * layer_stride_S (fp32 elements; 0 for
+// back to back), ring arrays l * layer_stride_ring slots past their bases.
+hipError_t launch_fold(const gdn_shape& sh, int num_layers, int64_t layer_stride_S,
+                       int64_t layer_stride_ring, float* S, const RingPtrs& r,
                        const int32_t* slot_idx, const CursorPtrs& c, int only_flagged,
                        hipStream_t stream);
 

@@ -35,6 +35,7 @@ struct RecParams {
     const int32_t* cache_base;
     const int32_t* is_flush;
     int only_flagged;
+    long long lsS, lsR;   // layer strides: fp32 elements of S, slots of the ring arrays
     // snapshot
     const void *q, *k, *v, *a, *b;
     const float *A_log, *dt_bias;
@@ -151,15 +152,15 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
     const int h = hv / (p.HV / p.H);
     const int L = p.L;
 
-    const size_t ring_slots = static_cast<size_t>(p.num_slots) * L;
-    float* Srow = p.S + static_cast<size_t>(layer) * p.num_slots * p.HV * p.V * K +
+    // layer l: S at l * lsS elements, the ring arrays l * lsR slots in
+    const size_t layer_recs = static_cast<size_t>(layer) * static_cast<size_t>(p.lsR) * L;
+    float* Srow = p.S + static_cast<size_t>(layer) * static_cast<size_t>(p.lsS) +
                   ((static_cast<size_t>(s) * p.HV + hv) * p.V + vrow) * K;
-    const st* rk = static_cast<const st*>(p.rawk) + static_cast<size_t>(layer) * ring_slots * p.H * K +
+    const st* rk = static_cast<const st*>(p.rawk) + layer_recs * p.H * K +
                    (static_cast<size_t>(s) * p.H + h) * L * K;
-    const st* rv = static_cast<const st*>(p.rawv) + static_cast<size_t>(layer) * ring_slots * p.HV * p.V +
+    const st* rv = static_cast<const st*>(p.rawv) + layer_recs * p.HV * p.V +
                    (static_cast<size_t>(s) * p.HV + hv) * L * p.V + tile * 16;
-    const size_t gofs = static_cast<size_t>(layer) * ring_slots * p.HV +
-                        (static_cast<size_t>(s) * p.HV + hv) * L;
+    const size_t gofs = layer_recs * p.HV + (static_cast<size_t>(s) * p.HV + hv) * L;
     const float* rg = p.rg + gofs;
     const float* rb = p.rb + gofs;
 
@@ -509,13 +510,17 @@ static RecParams base_params(const gdn_shape& sh)
     return p;
 }
 
-hipError_t launch_fold(const gdn_shape& sh, int num_layers, float* S, const RingPtrs& r,
+hipError_t launch_fold(const gdn_shape& sh, int num_layers, int64_t layer_stride_S,
+                       int64_t layer_stride_ring, float* S, const RingPtrs& r,
                        const int32_t* slot_idx, const CursorPtrs& c, int only_flagged,
                        hipStream_t stream)
 {
     if (sh.B == 0 || num_layers == 0)
         return hipSuccess;
     RecParams p = base_params(sh);
+    p.lsS = layer_stride_S > 0 ? layer_stride_S
+                               : static_cast<long long>(sh.num_slots) * sh.HV * sh.V * sh.K;
+    p.lsR = layer_stride_ring > 0 ? layer_stride_ring : sh.num_slots;
     p.S = S;
     p.rawk = r.rawk;
     p.rawv = r.rawv;

@@ -69,7 +69,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.gdn_spec_verify_ring.argtypes = [_sp] + [_vp] * 16 + [_i, _i, _vp, _vp]
         L.gdn_spec_verify_dcache.argtypes = [_sp] + [_vp] * 17 + [_i, _i, _vp, _vp]
-        L.gdn_exact_fold.argtypes = [_sp, _i] + [_vp] * 9 + [_i, _vp]
+        L.gdn_exact_fold.argtypes = [_sp, _i, ctypes.c_int64, ctypes.c_int64] + [_vp] * 9 + [_i, _vp]
         L.gdn_advance_cursors.argtypes = [_sp] + [_vp] * 6
         L.gdn_reset_cursors.argtypes = [_sp, _vp, ctypes.c_int32, ctypes.c_int32] + [_vp] * 4
         L.gdn_recurrent_verify_snapshot.argtypes = [_sp] + [_vp] * 17 + [_i, _vp]
@@ -145,12 +145,14 @@ def _window_checks(sh, q, k, v, a, b, A_log, dt_bias):
     _need("dt_bias", dt_bias, sh.HV, torch.float32)
 
 
-def _ring_checks(sh, rawk, rawv, g, beta, layers=1):
+def _ring_checks(sh, rawk, rawv, g, beta, layers=1, slot_stride=0):
+    """Ring arrays of `layers` layers placed `slot_stride` slots apart."""
     act = _act_dtype(sh)
-    _need("ring_rawk", rawk, layers * sh.num_slots * sh.H * sh.L * sh.K, act)
-    _need("ring_rawv", rawv, layers * sh.num_slots * sh.HV * sh.L * sh.V, act)
-    _need("ring_g", g, layers * sh.num_slots * sh.HV * sh.L, torch.float32)
-    _need("ring_beta", beta, layers * sh.num_slots * sh.HV * sh.L, torch.float32)
+    slots = (layers - 1) * (slot_stride or sh.num_slots) + sh.num_slots
+    _need("ring_rawk", rawk, slots * sh.H * sh.L * sh.K, act)
+    _need("ring_rawv", rawv, slots * sh.HV * sh.L * sh.V, act)
+    _need("ring_g", g, slots * sh.HV * sh.L, torch.float32)
+    _need("ring_beta", beta, slots * sh.HV * sh.L, torch.float32)
 
 
 def _cursor_checks(sh, *cur):
@@ -193,13 +195,17 @@ def gdn_spec_verify_dcache(shape, q, k, v, a, b, A_log, dt_bias, S, slot_idx, wr
     _check("gdn_spec_verify_dcache", st)
 
 
-def gdn_exact_fold(shape, num_layers, S, ring_rawk, ring_rawv, ring_g, ring_beta, slot_idx,
-                   write_pos, cache_base, is_flush, only_flagged, stream=None):
-    _need("S", S, num_layers * shape.num_slots * shape.HV * shape.V * shape.K, torch.float32)
-    _ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta, layers=num_layers)
+def gdn_exact_fold(shape, num_layers, layer_stride_S, layer_stride_ring, S, ring_rawk, ring_rawv,
+                   ring_g, ring_beta, slot_idx, write_pos, cache_base, is_flush, only_flagged,
+                   stream=None):
+    per_layer = shape.num_slots * shape.HV * shape.V * shape.K
+    _need("S", S, (num_layers - 1) * (layer_stride_S or per_layer) + per_layer, torch.float32)
+    _ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta, layers=num_layers,
+                 slot_stride=layer_stride_ring)
     _need("slot_idx", slot_idx, shape.B, torch.int32)
     _cursor_checks(shape, write_pos, cache_base, is_flush)
-    st = lib().gdn_exact_fold(ctypes.byref(shape), int(num_layers), _ptr(S), _ptr(ring_rawk),
+    st = lib().gdn_exact_fold(ctypes.byref(shape), int(num_layers), int(layer_stride_S),
+                              int(layer_stride_ring), _ptr(S), _ptr(ring_rawk),
                               _ptr(ring_rawv), _ptr(ring_g), _ptr(ring_beta), _ptr(slot_idx),
                               _ptr(write_pos), _ptr(cache_base), _ptr(is_flush),
                               int(only_flagged), _stream(stream))

@@ -79,6 +79,8 @@ def _load():
         lib.orc_write_ring.restype = None
         lib.orc_fold.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
         lib.orc_fold.restype = None
+        lib.orc_fill_dring.argtypes = [ctypes.POINTER(_Args), ctypes.c_int]
+        lib.orc_fill_dring.restype = None
         lib.orc_step.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, _dp,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double]
         lib.orc_step.restype = None
@@ -246,6 +248,18 @@ class OracleLayer:
         A, keep = self._args(cur, slot_idx, shape=sh)
         A.only_flagged = int(only_flagged)
         _load().orc_fold(ctypes.byref(A), nthreads or default_threads())
+        del keep
+
+    def fill_dring(self, cur, slot_idx, nthreads=None):
+        """Record the committed history's corrected deltas in the d ring in one
+        pass per (row, value head): what one-token d-cache verifies of the same
+        records would have stored."""
+        sh = self.shape.replace(B=len(slot_idx))
+        if self.d is None:
+            self.d = np.full((sh.num_slots, sh.HV, sh.L, sh.V), np.nan)
+        A, keep = self._args(cur, slot_idx, shape=sh)
+        A.rd = _ptr(self.d)
+        _load().orc_fill_dring(ctypes.byref(A), nthreads or default_threads())
         del keep
 
     def snapshot(self, slot_idx, win, cur=None, write_ring=False, nthreads=None):

@@ -245,6 +245,32 @@ static void snapshot_pair(const orc_args *A, int row, int hv, double *Sw)
     }
 }
 
+/* Deltas of the committed history, recorded in one pass: the state is
+ * stepped from the checkpoint through records 0..write_pos-1 and each step's
+ * corrected delta goes to the d ring at the record's physical position.  A
+ * one-token d-cache verify of record j replays the same j records from the
+ * same checkpoint before forming that delta, so a ring filled by such
+ * verifies holds these values. */
+static void fill_dring_pair(const orc_args *A, int row, int hv, double *Sw)
+{
+    const orc_shape *sh = &A->sh;
+    int s = A->slot[row];
+    if (!valid_slot(s, sh))
+        return;
+    int h = hv / (sh->HV / sh->H);
+    size_t VK = (size_t)sh->V * sh->K;
+    memcpy(Sw, A->S + ((size_t)s * sh->HV + hv) * VK, VK * sizeof(double));
+    int n = clamp_wp(A->wp[s], sh);
+    for (int j = 0; j < n; j++) {
+        int p = phys_pos(A->base[s], j, sh->L);
+        const double *kr = A->rawk + (((size_t)s * sh->H + h) * sh->L + p) * sh->K;
+        const double *vr = A->rawv + (((size_t)s * sh->HV + hv) * sh->L + p) * sh->V;
+        size_t gi = ((size_t)s * sh->HV + hv) * sh->L + p;
+        orc_step_d(Sw, sh->V, sh->K, kr, vr, A->rg[gi], A->rb[gi], sh->eps,
+                   A->rd + gi * sh->V);
+    }
+}
+
 /* --------------------------------------------------------------- threads */
 
 typedef void (*pair_fn)(const orc_args *, int, int, double *);
@@ -352,6 +378,11 @@ void orc_write_ring(orc_args *A)
 void orc_fold(orc_args *A, int nthreads)
 {
     run_pairs(A, fold_pair, nthreads);
+}
+
+void orc_fill_dring(orc_args *A, int nthreads)
+{
+    run_pairs(A, fill_dring_pair, nthreads);
 }
 
 void orc_snapshot(orc_args *A, int write_ring, int nthreads)

@@ -158,11 +158,12 @@ class Pair:
             cur_o.write_pos[:] = r
             osl = np.where(sl[self.orows] >= 0, self.oslots, -1).astype(np.int32)
             wo = helpers.window_rows(w, self.orows, 1)
-            if dcache:
-                self.orc.verify(cur_o, osl, helpers.win_f64(wo, self.act), write_ring=True,
-                                fold_flagged=False, T=1, dcache=True)
-            else:
-                self.orc.write_ring(cur_o, osl, helpers.win_f64(wo, self.act), T=1)
+            self.orc.write_ring(cur_o, osl, helpers.win_f64(wo, self.act), T=1)
+        if dcache:
+            # the deltas those one-token d-cache verifies record, in one pass
+            # per (row, value head) (a pinned identity of the oracle)
+            cur_o.write_pos[:] = wp[gslots]
+            self.orc.fill_dring(cur_o, self.oslots)
         torch.cuda.synchronize()
         self.cur = CursorState(wp.copy(), base.copy(),
                                (wp + 2 * shape.max_spec > shape.L).astype(np.int32))

@@ -35,3 +35,25 @@ def max_rel(x, ref):
     ref = np.asarray(ref, dtype=np.float64)
     den = np.max(np.abs(ref))
     return float(np.max(np.abs(x - ref)) / (den if den > 0 else 1.0))
+
+
+def elem_rel(x, ref, floor: float = 1e-3):
+    """max over elements of |x - ref| / (|ref| + floor * max |ref|): the
+    elementwise relative error, with a floor so that values near zero are
+    judged against the tensor's scale rather than their own."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.max(np.abs(ref))
+    den = np.abs(ref) + floor * (scale if scale > 0 else 1.0)
+    return float(np.max(np.abs(x - ref) / den))
+
+
+# Lines collected by the tests and printed once at the end of the session
+# (see conftest.py), so that figures such as drift curves and full-size error
+# metrics appear in the run's output even when pytest captures test output.
+REPORT: list = []
+
+
+def report(line: str) -> None:
+    print(line, flush=True)
+    REPORT.append(line)

@@ -72,7 +72,7 @@ def test_invalid_shapes_are_rejected(override, status):
     L = gv.lib()
     n = None
     assert L.gdn_spec_verify_ring(ctypes.byref(sh), *([n] * 16), 1, 1, n, n) == status
-    assert L.gdn_exact_fold(ctypes.byref(sh), 1, *([n] * 9), 1, n) == status
+    assert L.gdn_exact_fold(ctypes.byref(sh), 1, 0, 0, *([n] * 9), 1, n) == status
     assert L.gdn_advance_cursors(ctypes.byref(sh), *([n] * 6)) == status
     assert L.gdn_reset_cursors(ctypes.byref(sh), n, 0, 0, n, n, n, n) == status
     assert L.gdn_recurrent_verify_snapshot(ctypes.byref(sh), *([n] * 17), 0, n) == status
@@ -93,7 +93,7 @@ def test_null_and_misaligned_pointers_are_rejected():
     # output aliasing an input
     args = [good] * 16
     assert L.gdn_spec_verify_ring(ctypes.byref(sh), *args, 1, 1, good, n) == gv.GDN_EINVAL
-    assert L.gdn_exact_fold(ctypes.byref(sh), 0, *([good] * 9), 1, n) == gv.GDN_EINVAL
+    assert L.gdn_exact_fold(ctypes.byref(sh), 0, 0, 0, *([good] * 9), 1, n) == gv.GDN_EINVAL
     assert L.gdn_reset_cursors(ctypes.byref(sh), good, -1, 0, good, good, good, n) == gv.GDN_EINVAL
     assert L.gdn_advance_cursors(ctypes.byref(sh), good, n, good, good, good, n) == gv.GDN_EINVAL
     assert L.gdn_snapshot_commit(ctypes.byref(sh), good, good, n, good, n) == gv.GDN_EINVAL
@@ -123,3 +123,37 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(gv, "_LIB_PATH", "/nonexistent/libgdnverify.so")
     with pytest.raises(RuntimeError, match="missing"):
         gv.lib()
+
+
+def test_fold_layer_strides_are_validated():
+    # per-layer placement: fp32 elements of S, slots of the ring arrays; 0
+    # means back to back.  Negative, overlapping or misaligned strides are
+    # refused on the host.
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"])
+    L = gv.lib()
+    per_S = sh.num_slots * sh.HV * sh.V * sh.K
+    ptrs = [ctypes.c_void_p((3 + i) << 20) for i in range(9)]
+    n = None
+    for nl, ls, lr in ((2, -4, 0), (2, 0, -1), (3, per_S - 4, 0), (3, 0, sh.num_slots - 1),
+                       (2, per_S + 2, 0), (1, -4, 0)):
+        assert L.gdn_exact_fold(ctypes.byref(sh), nl, ls, lr, *ptrs, 1, n) == gv.GDN_EINVAL, (nl, ls, lr)
+
+
+def test_bf16_gate_words_stay_inside_the_buffers():
+    # the ring verify reads bf16 gate inputs as aligned words of two
+    # activations: misaligned a/b are refused, and so is an odd B*T*HV
+    # (its last word would reach past the end of a and b)
+    L = gv.lib()
+    n = None
+    base = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"])
+    args = [ctypes.c_void_p((3 + i) << 20) for i in range(16)]
+    out = ctypes.c_void_p(40 << 20)
+    odd = base.replace(B=3, T=1, H=1, HV=1, max_spec_len=1, L=64)
+    assert gv.gdn_validate_shape(odd) == gv.GDN_OK
+    assert L.gdn_spec_verify_ring(ctypes.byref(odd), *args, 1, 1, out, n) == gv.GDN_EUNSUPPORTED
+    mis = list(args)
+    mis[3] = ctypes.c_void_p((6 << 20) + 2)      # a: 2-byte aligned only
+    assert L.gdn_spec_verify_ring(ctypes.byref(base), *mis, 1, 1, out, n) == gv.GDN_EINVAL
+    # fp32 activations read a and b element by element: an odd count is fine
+    odd32 = odd.replace(act=gv.GDN_F32)
+    assert gv.gdn_validate_shape(odd32) == gv.GDN_OK

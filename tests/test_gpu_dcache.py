@@ -169,39 +169,42 @@ def test_dcache_ring_write_is_a_side_channel_and_padding_rows_are_inert():
         assert np.array_equal(rd1[P.slots[r]], rd0[P.slots[r]]), r
 
 
-def test_dcache_bandwidth_batch_b256_sampled_rows():
-    """Two steps at B=256 / 512 slots, fold then d-cache verify as the benchmark
-    launches them; the oracle follows eight rows, two of them flagged."""
+def test_dcache_bandwidth_batch_b256_all_rows():
+    """Four steps at B=256 / 512 slots, fold then d-cache verify as the
+    benchmark launches them; every row and value head is compared with the
+    oracle: outputs, checkpoints (folded ones also against a tight internal
+    bar) and the deltas recorded this step."""
     shape = synth.CONFIGS["qwen3next_b256"]
     rng = synth.make_rng(1702)
     slots = synth.slot_choice(rng, shape)
     cd = synth.random_cursors(rng, shape)
-    fl0 = (cd.write_pos + 2 * shape.max_spec > shape.L)[slots]
-    flagged = np.flatnonzero(fl0)
-    pick = set(rng.choice(shape.B, 6, replace=False).tolist()) | set(flagged[:2].tolist())
     P = Pair(shape, 1702, slots=slots, wp_by_slot=cd.write_pos, base_by_slot=cd.cache_base,
-             oracle_rows=np.array(sorted(pick)), dcache=True)
+             dcache=True)
     tol = TOL[shape.act]
     g = P.gpu
-    gslots = P.slots[P.orows]
-    for step_i in range(2):
+    sel = torch.from_numpy(P.slots.astype(np.int64)).to("cuda:0")
+    for step_i in range(4):
         win = P.window()
         o = g.new_out()
         S_before = g.S.clone()
         fl = P.cur.is_flush[P.slots].astype(bool)
         wp_now, base_now = P.ocur.write_pos.copy(), P.ocur.cache_base.copy()
-        gv.gdn_exact_fold(g.gs, 1, g.S, *g.ring(), P.dslots, *P.dcur, 1)
+        gv.gdn_exact_fold(g.gs, 1, 0, 0, g.S, *g.ring(), P.dslots, *P.dcur, 1)
         g.verify_dcache(P.dcur, P.dslots, DevWindow(win, shape.act), o, write_ring=1,
                         fold_flagged=0)
         ref = P.oracle_verify(win, dcache=True)
-        err = helpers.max_rel(P.gpu_out_rows(o), ref)
+        got_o = P.gpu_out_rows(o)
+        err = helpers.max_rel(got_o, ref)
+        eerr = helpers.elem_rel(got_o, ref)
         assert bool(torch.isfinite(o.float()).all())
         keep = torch.from_numpy(P.slots[~fl].astype(np.int64)).to("cuda:0")
         assert torch.equal(g.S.index_select(0, keep), S_before.index_select(0, keep))
         del S_before
-        sel = torch.from_numpy(gslots.astype(np.int64)).to("cuda:0")
-        serr = helpers.max_rel(host_f64(g.S.index_select(0, sel)), P.orc.S)
-        # the deltas this step recorded for the followed rows
+        Sg = host_f64(g.S.index_select(0, sel))
+        serr = helpers.max_rel(Sg, P.orc.S)
+        ferr = helpers.max_rel(Sg[fl], P.orc.S[fl]) if fl.any() else 0.0
+        del Sg
+        # the deltas this step recorded, for every row
         rd = host_f64(g.rd.index_select(0, sel))
         got, want = [], []
         for r in range(len(P.orows)):
@@ -209,10 +212,14 @@ def test_dcache_bandwidth_batch_b256_sampled_rows():
                 p = (int(base_now[r]) + int(wp_now[r]) + t) % shape.L
                 got.append(rd[r, :, p])
                 want.append(P.orc.d[r, :, p])
+        del rd
         derr = helpers.max_rel(np.stack(got), np.stack(want))
-        say(f"d-cache b256 step {step_i}: max_rel(o)={err:.2e} max_rel(S)={serr:.2e} "
-            f"max_rel(d)={derr:.2e}, {int(fl.sum())} rows folded")
+        helpers.report(f"d-cache b256 step {step_i}: {shape.B} rows x {shape.HV} heads, "
+                       f"max_rel(o) = {err:.2e}, elementwise rel(o) = {eerr:.2e}, "
+                       f"max_rel(S) = {serr:.2e}, folded rows ({int(fl.sum())}) "
+                       f"max_rel(S) = {ferr:.2e}, max_rel(d) = {derr:.2e}")
         assert err <= tol and serr <= tol and derr <= tol
+        assert ferr <= 1e-5, ferr
         acc = P.rng.integers(0, shape.T + 1, size=shape.B).astype(np.int32)
         gv.gdn_advance_cursors(g.gs, P.dslots, dev_i32(acc), *P.dcur)
         advance(P.cur, P.slots, acc, shape.L, shape.T, shape.max_spec)

@@ -277,11 +277,22 @@ def test_cache_base_shift_gives_identical_outputs():
 
 # ------------------------------------------------ snapshot baseline and fold
 
-@pytest.mark.parametrize("name", ["qwen3next_b32", "qwen3next_b256"])
+SNAPSHOT_SHAPES = {
+    "qwen3next_b32": synth.CONFIGS["qwen3next_b32"],
+    "qwen3next_b256": synth.CONFIGS["qwen3next_b256"],
+    # fp32 activations at the widest key: the snapshot kernel's largest LDS
+    "f32_k256": synth.LayerShape(B=3, T=4, H=2, HV=4, K=256, V=32, L=64, max_spec=4,
+                                 num_slots=5, act="f32"),
+    "f32_k64_t8": synth.LayerShape(B=4, T=8, H=1, HV=2, K=64, V=48, L=32, max_spec=8,
+                                   num_slots=6, act="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(SNAPSHOT_SHAPES))
 def test_snapshot_matches_oracle_and_fold_reproduces_it_bitwise(name):
     # at B=256 every row is folded (rows spread over all waves of the fold's
     # row compaction); the oracle follows a sample of rows
-    shape = synth.CONFIGS[name]
+    shape = SNAPSHOT_SHAPES[name]
     wp0 = np.zeros(shape.num_slots, np.int32)            # empty history everywhere
     orows = None if shape.B <= 32 else np.sort(synth.make_rng(2401).choice(shape.B, 8, replace=False))
     P = Pair(shape, 2400, wp_by_slot=wp0, oracle_rows=orows)
@@ -314,7 +325,7 @@ def test_snapshot_matches_oracle_and_fold_reproduces_it_bitwise(name):
     wp[P.slots] = acc
     fl = np.ones(shape.num_slots, np.int32)
     S_fold = g.S.clone()
-    gv.gdn_exact_fold(gs, 1, S_fold, *g.ring(), P.dslots, dev_i32(wp), P.dcur[1], dev_i32(fl), 1)
+    gv.gdn_exact_fold(gs, 1, 0, 0, S_fold, *g.ring(), P.dslots, dev_i32(wp), P.dcur[1], dev_i32(fl), 1)
     # and the snapshot path's own commit
     S_commit = g.S.clone()
     gv.gdn_snapshot_commit(gs, snap, P.dslots, dev_i32(acc), S_commit)
@@ -340,7 +351,7 @@ def test_exact_fold_multi_layer_matches_oracle():
     ring = [cat([P.gpu.ring()[i] for P in layers]) for i in range(4)]
     fl = np.ones(shape.num_slots, np.int32)
     P0 = layers[0]
-    gv.gdn_exact_fold(P0.gpu.gs, 3, S, *ring, P0.dslots, dev_i32(wp), dev_i32(base),
+    gv.gdn_exact_fold(P0.gpu.gs, 3, 0, 0, S, *ring, P0.dslots, dev_i32(wp), dev_i32(base),
                       dev_i32(fl), 1)
     Sh = host_f64(S).reshape(3, shape.num_slots, shape.HV, shape.V, shape.K)
     for l, P in enumerate(layers):
@@ -354,6 +365,48 @@ def test_exact_fold_multi_layer_matches_oracle():
         assert np.array_equal(Sh[l][untouched], P.params.S0[untouched].astype(np.float64))
 
 
+def test_exact_fold_layers_at_strides():
+    # three layers of a pool laid out [layer][slot][...] with more slots per
+    # layer than the shape uses: S placed layer_stride_S elements apart, the
+    # ring arrays layer_stride_ring slots apart.  One launch folds all three;
+    # each layer matches the oracle and nothing between the layers is written.
+    shape = synth.CONFIGS["qwen3next_b32"].replace(B=8, num_slots=12)
+    rng = synth.make_rng(2550)
+    slots = rng.permutation(shape.num_slots)[: shape.B].astype(np.int32)
+    wp = rng.integers(0, shape.L - shape.T + 1, size=shape.num_slots).astype(np.int32)
+    base = rng.integers(0, shape.L, size=shape.num_slots).astype(np.int32)
+    layers = [Pair(shape, 2551 + l, wp_by_slot=wp, base_by_slot=base, slots=slots)
+              for l in range(3)]
+    per_S = shape.num_slots * shape.HV * shape.V * shape.K
+    ls_S = per_S + 4 * 777                      # 16-byte aligned gap after each layer
+    ls_R = shape.num_slots + 5                  # five unused slots after each layer's ring
+    S = torch.full((3 * ls_S,), -1234.5, dtype=torch.float32, device="cuda:0")
+    g0 = layers[0].gpu
+    per_slot = [t[0].numel() for t in g0.ring()]
+    ring = [torch.zeros(3 * ls_R * n, dtype=t.dtype, device="cuda:0")
+            for t, n in zip(g0.ring(), per_slot)]
+    for l, P in enumerate(layers):
+        S[l * ls_S: l * ls_S + per_S].copy_(P.gpu.S.reshape(-1))
+        for buf, t, n in zip(ring, P.gpu.ring(), per_slot):
+            buf[l * ls_R * n: l * ls_R * n + t.numel()].copy_(t.reshape(-1))
+    fl = np.ones(shape.num_slots, np.int32)
+    gv.gdn_exact_fold(g0.gs, 3, ls_S, ls_R, S, *ring, layers[0].dslots, dev_i32(wp),
+                      dev_i32(base), dev_i32(fl), 1)
+    Sh = host_f64(S)
+    for l, P in enumerate(layers):
+        ocur = CursorState(P.ocur.write_pos.copy(), P.ocur.cache_base.copy(),
+                           np.ones(len(P.oslots), np.int32))
+        P.orc.fold(ocur, P.oslots, only_flagged=True)
+        Sl = Sh[l * ls_S: l * ls_S + per_S].reshape(shape.num_slots, shape.HV, shape.V, shape.K)
+        err = helpers.max_rel(Sl[slots], P.orc.S)
+        say(f"strided fold layer {l}: max_rel(S)={err:.2e}")
+        assert err <= 1e-5
+        untouched = np.setdiff1d(np.arange(shape.num_slots), slots)
+        assert np.array_equal(Sl[untouched], P.params.S0[untouched].astype(np.float64))
+        gap = Sh[l * ls_S + per_S: (l + 1) * ls_S]
+        assert np.all(gap == -1234.5), l
+
+
 # ------------------------------------------------------------ shape sweep
 
 SWEEP = [
@@ -364,6 +417,10 @@ SWEEP = [
     dict(B=2, T=4, H=4, HV=8, K=128, V=128, L=64, max_spec=4, num_slots=3, act="f32"),
     dict(B=2, T=16, H=2, HV=4, K=64, V=64, L=128, max_spec=16, num_slots=3, act="bf16"),
     dict(B=6, T=5, H=3, HV=6, K=64, V=80, L=16, max_spec=8, num_slots=7, act="f32"),
+    # fp32 activations with a 128-record ring (32-row value tiles, the
+    # largest verify LDS) and at the widest key
+    dict(B=3, T=8, H=2, HV=4, K=128, V=64, L=128, max_spec=8, num_slots=4, act="f32"),
+    dict(B=2, T=4, H=2, HV=4, K=256, V=32, L=64, max_spec=4, num_slots=3, act="f32"),
 ]
 
 

@@ -343,6 +343,28 @@ def test_dcache_ring_write_lands_at_write_pos():
     np.testing.assert_array_equal(np.nan_to_num(layer.d[same]), np.nan_to_num(before[same]))
 
 
+def test_one_pass_dring_fill_equals_one_token_verifies():
+    # the one-pass fill (used to pre-fill large d rings in the GPU tests)
+    # stores exactly the deltas that one-token d-cache verifies recorded
+    shape = _tiny_shape()
+    wp = np.array([0, 5, 13, 9, 1], dtype=np.int32)
+    base = np.array([3, 14, 9, 0, 15], dtype=np.int32)
+    layer, cur, slots, _ = _prefilled_layer_dcache(shape, 27, wp, base, "low_decay")
+    other = oracle.OracleLayer(shape, layer.A_log, layer.dt_bias, layer.S)
+    for n in ("rawk", "rawv", "g", "beta"):
+        setattr(other, n, getattr(layer, n).copy())
+    other.fill_dring(cur, slots)
+    for s in slots:
+        for j in range(int(wp[s])):
+            p = phys(base[s], j, shape.L)
+            np.testing.assert_allclose(other.d[s, :, p], layer.d[s, :, p], rtol=1e-14, atol=1e-16)
+            assert not np.isnan(other.d[s, :, p]).any()
+    # nothing past the committed records is written
+    for s in slots:
+        for j in range(int(wp[s]), shape.L):
+            assert np.isnan(other.d[s, :, phys(base[s], j, shape.L)]).all()
+
+
 # ------------------------------------------------------- structural invariants
 
 def test_causality_later_tokens_do_not_change_earlier_outputs():
