@@ -96,6 +96,10 @@ __device__ __forceinline__ void store_cols_f32(float* row, int c, const float (&
             f32x4{x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
 }
 
+// Threads that load a batch's gates and betas (they may also load values).
+constexpr int kGateT = 128;
+
+
 // Records of the fold are staged through LDS in batches of kFoldBatch,
 // double-buffered: the loads of batch i+1 are in flight while the sequential
 // steps of batch i run from LDS.  Each thread loads the raw key columns it
@@ -103,16 +107,18 @@ __device__ __forceinline__ void store_cols_f32(float* row, int c, const float (&
 // so raw keys never pass through LDS.
 constexpr int kFoldBatch = 16;
 
-template <class Act, int K>
+// RPG state rows per 16-lane group: a tile is 16 RPG value rows.  Several
+// rows per lane give each wave independent step chains to interleave.
+template <class Act, int K, int RPG = 1>
 struct FoldStage {
-    static constexpr int VU = 16 * Act::bytes / 16;           // units of 16 values
+    static constexpr int VU = RPG * 16 * Act::bytes / 16;     // 16-byte units of a record's tile values
     static constexpr int VUB = kFoldBatch * VU;
     typedef typename std::conditional<Act::bytes == 4, uint4, uint2>::type KRaw;   // 4 activations
 };
 
-template <class Act, int K>
+template <class Act, int K, int RPG = 1>
 struct FoldShared {
-    uint4 vbuf[2][FoldStage<Act, K>::VUB];          // this tile's 16 values per record
+    uint4 vbuf[2][FoldStage<Act, K, RPG>::VUB];     // this tile's values per record
     float gbuf[2][kFoldBatch], bbuf[2][kFoldBatch];  // decay e^g and beta
     float khs[2][kFoldBatch][K];                     // normalised keys
 };
@@ -129,14 +135,16 @@ __device__ __forceinline__ f32x4 widen4(uint2 u)
                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
 }
 
-// Fold of one work item: the n committed records of slot s into 16 rows
-// (tile) of one layer's value head hv.  Called uniformly by the workgroup.
-template <class Act, int K>
-__device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int n, int base,
+// Fold of one work item: the n committed records of slot s into the 16 RPG
+// rows (tile) of one layer's value head hv.  Called uniformly by the
+// workgroup.
+template <class Act, int K, int RPG = 1, class P = const RecParams>
+__device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int base,
                           int layer, int hv, int tile)
 {
     using st = typename Act::storage;
-    using FS = FoldStage<Act, K>;
+    using FS = FoldStage<Act, K, RPG>;
+    constexpr int TR = 16 * RPG;                   // rows of a tile
     using KRaw = typename FS::KRaw;
     constexpr int EPL = K / 16;
     constexpr int RB = kFoldBatch;
@@ -147,19 +155,19 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, grp = lane >> 4;
-    const int row16 = w * 4 + grp;                 // row within the 16-row tile
-    const int vrow = tile * 16 + row16;
+    const int row16 = w * 4 + grp;                 // lane group: rows row16 + 16 j of the tile
+    const int vrow = tile * TR + row16;
     const int h = hv / (p.HV / p.H);
     const int L = p.L;
 
     // layer l: S at l * lsS elements, the ring arrays l * lsR slots in
     const size_t layer_recs = static_cast<size_t>(layer) * static_cast<size_t>(p.lsR) * L;
     float* Srow = p.S + static_cast<size_t>(layer) * static_cast<size_t>(p.lsS) +
-                  ((static_cast<size_t>(s) * p.HV + hv) * p.V + vrow) * K;
+                  ((static_cast<size_t>(s) * p.HV + hv) * p.V + vrow) * K;   // + 16 j K for row j
     const st* rk = static_cast<const st*>(p.rawk) + layer_recs * p.H * K +
                    (static_cast<size_t>(s) * p.H + h) * L * K;
     const st* rv = static_cast<const st*>(p.rawv) + layer_recs * p.HV * p.V +
-                   (static_cast<size_t>(s) * p.HV + hv) * L * p.V + tile * 16;
+                   (static_cast<size_t>(s) * p.HV + hv) * L * p.V + tile * TR;
     const size_t gofs = layer_recs * p.HV + (static_cast<size_t>(s) * p.HV + hv) * L;
     const float* rg = p.rg + gofs;
     const float* rb = p.rb + gofs;
@@ -186,8 +194,9 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
                 const int ph = (base + j) & (L - 1);
                 vreg = reinterpret_cast<const uint4*>(rv + static_cast<size_t>(ph) * p.V)[tid % FS::VU];
             }
-        } else if (tid >= 128 && tid < 128 + 2 * RB) {
-            const int r = tid - 128;
+        }
+        if (tid >= kGateT && tid < kGateT + 2 * RB) {
+            const int r = tid - kGateT;
             const int j = bi * RB + (r % RB);
             if (j < n) {
                 const int ph = (base + j) & (L - 1);
@@ -196,10 +205,10 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
         }
     };
     auto commit = [&](int buf) {
-        if (tid < FS::VUB) {
+        if (tid < FS::VUB)
             vbuf[buf][tid] = vreg;
-        } else if (tid >= 128 && tid < 128 + 2 * RB) {
-            const int r = tid - 128;
+        if (tid >= kGateT && tid < kGateT + 2 * RB) {
+            const int r = tid - kGateT;
             if (r < RB)
                 gbuf[buf][r] = expf(greg);
             else
@@ -226,8 +235,10 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
     };
 
     issue(0);
-    float sv[EPL];
-    load_cols_f32<K>(Srow, c, sv);
+    float sv[RPG][EPL];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+        load_cols_f32<K>(Srow + static_cast<size_t>(16 * j) * K, c, sv[j]);
     commit(0);
     prep(0, min(RB, n));
     __syncthreads();
@@ -242,7 +253,10 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
         for (int jj = 0; jj < cnt; ++jj) {
             float kh[EPL];
             load_cols_f32<K>(sh.khs[buf][jj], c, kh);
-            step_row<EPL>(sv, kh, Act::load(vb + jj * 16 + row16), gbuf[buf][jj], bbuf[buf][jj]);
+            const float dec = gbuf[buf][jj], bta = bbuf[buf][jj];
+#pragma unroll
+            for (int j = 0; j < RPG; ++j)
+                step_row<EPL>(sv[j], kh, Act::load(vb + jj * TR + 16 * j + row16), dec, bta);
         }
         // buffer buf ^ 1 was last read by the previous batch's steps, which
         // every thread finished before the barrier that ended that batch
@@ -253,7 +267,9 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
         __syncthreads();
     }
 
-    store_cols_f32<K>(Srow, c, sv);
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+        store_cols_f32<K>(Srow + static_cast<size_t>(16 * j) * K, c, sv[j]);
 }
 
 // Persistent fold: every workgroup compacts the rows to fold (in chunks of
@@ -261,16 +277,16 @@ __device__ void fold_item(const RecParams& p, FoldShared<Act, K>& sh, int s, int
 // head, 16-row tile).  Rows with nothing to fold cost no workgroup.
 constexpr int kFoldRows = 512;
 
-template <class Act, int K>
+template <class Act, int K, int RPG>
 __global__ __launch_bounds__(256) void fold_kernel(const RecParams p, int num_layers)
 {
-    __shared__ FoldShared<Act, K> sh;
+    __shared__ FoldShared<Act, K, RPG> sh;
     __shared__ int rows[kFoldRows];
     __shared__ int wcount[4];
     __shared__ int nrows;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int tiles = p.V / 16;
+    const int tiles = p.V / (16 * RPG);
     const int per_row = num_layers * p.HV * tiles;
     for (int c0 = 0; c0 < p.B; c0 += kFoldRows) {
         const int cend = min(c0 + kFoldRows, p.B);
@@ -308,8 +324,8 @@ __global__ __launch_bounds__(256) void fold_kernel(const RecParams p, int num_la
             const int tile = rem % tiles;
             const int lh = rem / tiles;              // layer * HV + hv
             const int s = p.slot_idx[row];
-            fold_item<Act, K>(p, sh, s, clamp_wp(p.write_pos[s], p.L, p.T), p.cache_base[s],
-                              lh / p.HV, lh % p.HV, tile);
+            fold_item<Act, K, RPG>(p, sh, s, clamp_wp(p.write_pos[s], p.L, p.T), p.cache_base[s],
+                                   lh / p.HV, lh % p.HV, tile);
         }
         __syncthreads();
     }
@@ -462,23 +478,38 @@ __global__ __launch_bounds__(256) void snapshot_commit_kernel(int T, int num_slo
     S[static_cast<size_t>(s) * n4 + i] = snap[(static_cast<size_t>(b) * T + acc - 1) * n4 + i];
 }
 
-template <class Act>
-static hipError_t launch_fold_act(const gdn_shape& sh, int num_layers, const RecParams& p,
+template <class Act, int RPG>
+static hipError_t launch_fold_rpg(const gdn_shape& sh, int num_layers, const RecParams& p,
                                   hipStream_t stream)
 {
     // persistent grid of 2048 workgroups, never more than items.  That is more
     // than fit at once (7 per compute unit at K = 128): the ones that wait for
     // a slot balance the load.  A grid of exactly the resident workgroups
     // was slower both for a few flagged rows and for folding every row.
-    const long long items = static_cast<long long>(sh.B) * num_layers * sh.HV * (sh.V / 16);
+    const long long items = static_cast<long long>(sh.B) * num_layers * sh.HV * (sh.V / (16 * RPG));
     const unsigned grid = static_cast<unsigned>(items < 2048 ? items : 2048);
     switch (sh.K) {
-    case 64: hipLaunchKernelGGL((fold_kernel<Act, 64>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
-    case 128: hipLaunchKernelGGL((fold_kernel<Act, 128>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
-    case 256: hipLaunchKernelGGL((fold_kernel<Act, 256>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
+    case 64: hipLaunchKernelGGL((fold_kernel<Act, 64, RPG>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
+    case 128: hipLaunchKernelGGL((fold_kernel<Act, 128, RPG>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
+    case 256: hipLaunchKernelGGL((fold_kernel<Act, 256, RPG>), dim3(grid), dim3(256), 0, stream, p, num_layers); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// Four state rows per lane group wherever the value rows allow 64-row tiles:
+// the same time as one row per group when a few flagged rows are folded
+// (56.8 against 56.5 us for 13 rows at the B=256 workload), 20% less when
+// every row is (448 against 563 us), and the same bits.
+template <class Act>
+static hipError_t launch_fold_act(const gdn_shape& sh, int num_layers, const RecParams& p,
+                                  hipStream_t stream)
+{
+    if (sh.V % 64 == 0)
+        return launch_fold_rpg<Act, 4>(sh, num_layers, p, stream);
+    if (sh.V % 32 == 0)
+        return launch_fold_rpg<Act, 2>(sh, num_layers, p, stream);
+    return launch_fold_rpg<Act, 1>(sh, num_layers, p, stream);
 }
 
 template <class Act>
