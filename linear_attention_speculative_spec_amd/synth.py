@@ -215,6 +215,48 @@ def ring_garbage_template(rng, shape: LayerShape, num_layers: int = 1) -> dict:
     }
 
 
+# ------------------------------------------------ KDA (per-channel gate)
+#
+# The KDA layer's gate input a and bias dt_bias carry one value per key
+# channel: a [B*T, HV, K] ~ N(0, 1) and dt_bias [HV, K] ~ N(0, 0.1); A_log stays
+# one value per value head.  The ring's gate records hold K fp32 values.
+
+
+def kda_layer_params(rng, shape: LayerShape, variant: str = "base") -> LayerParams:
+    lo, hi = (1e-3, 1e-2) if variant == "low_decay" else (1.0, 16.0)
+    A_log = np.log(rng.uniform(lo, hi, size=shape.HV)).astype(np.float32)
+    dt_bias = _normal(rng, (shape.HV, shape.K), 0.0, 0.1)
+    S0 = _normal(rng, (shape.num_slots, shape.HV, shape.V, shape.K), 0.0, 0.02)
+    return LayerParams(A_log=A_log, dt_bias=dt_bias, S0=S0)
+
+
+def kda_window(rng, shape: LayerShape, variant: str = "base", n_tok: int | None = None) -> Window:
+    n = shape.B * shape.T if n_tok is None else n_tok
+    bmean = 4.0 if variant == "beta_high" else 0.0
+    act = shape.act
+    return Window(
+        q=as_act(_normal(rng, (n, shape.H, shape.K)), act),
+        k=as_act(_normal(rng, (n, shape.H, shape.K)), act),
+        v=as_act(_normal(rng, (n, shape.HV, shape.V)), act),
+        a=as_act(_normal(rng, (n, shape.HV, shape.K)), act),
+        b=as_act(_normal(rng, (n, shape.HV), bmean), act),
+    )
+
+
+def kda_history_windows(rng, shape: LayerShape, n_records: int, variant: str = "base") -> list:
+    """Raw KDA records for pre-filling rings, one single-token window each."""
+    return [kda_window(rng, shape, variant, n_tok=shape.B) for _ in range(n_records)]
+
+
+def kda_ring_garbage_template(rng, shape: LayerShape) -> dict:
+    """As ring_garbage_template, with K gate values per record."""
+    t = ring_garbage_template(rng, shape)
+    n = shape.num_slots * shape.HV * shape.L * shape.K
+    g = (np.uint32(0x7FC00000) | rng.integers(1, 0x3FFFFF, size=n, dtype=np.uint32)).astype(np.uint32)
+    t["g"] = g.view(np.float32).reshape(shape.num_slots, shape.HV, shape.L, shape.K)
+    return t
+
+
 class DeviceWindows:
     """Seeded draft windows drawn on the device, for long runs.
 

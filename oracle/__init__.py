@@ -6,6 +6,7 @@ the HIP path; the only thing both sides share is the seeded input generator.
 
 * ``gdn_oracle.c``  - plain fp64 recurrence: gating, l2 norm, the gated delta
   step, verify (history replay then window), exact fold, snapshot baseline.
+* ``kda_oracle.c``  - the same for the per-channel-gate (KDA) layer.
 * ``cursors.py``    - the integer ring/cursor algorithm.
 * ``closed_form.py``- the chunked closed form, used only to pin the recurrence.
 
@@ -30,6 +31,7 @@ from .cursors import CursorState, advance, reset  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
+_SRC_KDA = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libgdnoracle.so")
 _lib = None
 
@@ -39,7 +41,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, _SRC_KDA, "-o", tmp,
+                               "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -64,6 +67,15 @@ class _Args(ctypes.Structure):
                 ("fold_flagged", ctypes.c_int), ("only_flagged", ctypes.c_int),
                 ("pair_row", _ip), ("pair_hv", _ip), ("n_pairs", ctypes.c_int),
                 ("dwin", _dp), ("rd", _dp)]
+
+
+class _KArgs(ctypes.Structure):
+    _fields_ = [("sh", _Shape),
+                ("S", _dp), ("rawk", _dp), ("rawv", _dp), ("rg", _dp), ("rb", _dp),
+                ("wp", _ip), ("base", _ip), ("flush", _ip), ("slot", _ip),
+                ("q", _dp), ("k", _dp), ("v", _dp), ("a", _dp), ("b", _dp),
+                ("A_log", _dp), ("dt_bias", _dp), ("o", _dp),
+                ("fold_flagged", ctypes.c_int), ("only_flagged", ctypes.c_int)]
 
 
 def _load():
@@ -95,6 +107,23 @@ def _load():
                                     ctypes.c_double, _dp]
         lib.orc_readout.restype = None
         assert lib.orc_args_size() == ctypes.sizeof(_Args)
+        for fn in ("kda_verify",):
+            getattr(lib, fn).argtypes = [ctypes.POINTER(_KArgs), ctypes.c_int, ctypes.c_int]
+            getattr(lib, fn).restype = None
+        lib.kda_write_ring.argtypes = [ctypes.POINTER(_KArgs)]
+        lib.kda_write_ring.restype = None
+        lib.kda_fold.argtypes = [ctypes.POINTER(_KArgs), ctypes.c_int]
+        lib.kda_fold.restype = None
+        lib.kda_gate.argtypes = [_dp, ctypes.c_double, ctypes.c_double, _dp, ctypes.c_int,
+                                 ctypes.c_double, _dp, _dp]
+        lib.kda_gate.restype = None
+        lib.kda_step.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp,
+                                 ctypes.c_double, ctypes.c_double]
+        lib.kda_step.restype = None
+        lib.kda_readout.argtypes = [_dp, ctypes.c_int, ctypes.c_int, _dp, ctypes.c_double,
+                                    ctypes.c_double, _dp]
+        lib.kda_readout.restype = None
+        assert lib.kda_args_size() == ctypes.sizeof(_KArgs)
         _lib = lib
     return _lib
 
@@ -273,3 +302,96 @@ class OracleLayer:
         _load().orc_snapshot(ctypes.byref(A), int(write_ring), nthreads or default_threads())
         del keep
         return o, snap
+
+
+# ------------------------------------------------------ KDA (per-channel gate)
+
+def kda_gate(a, b: float, A_log: float, dt_bias, threshold: float = 20.0):
+    """(g [K], beta) of one token and value head with a per-channel gate."""
+    a, dt_bias = _f64(a), _f64(dt_bias)
+    g = np.empty(a.size)
+    beta = ctypes.c_double()
+    _load().kda_gate(_ptr(a), b, A_log, _ptr(dt_bias), a.size, threshold, _ptr(g), ctypes.byref(beta))
+    return g, beta.value
+
+
+def kda_step(S, k_raw, v, g, beta: float, eps: float = 1e-6) -> np.ndarray:
+    """One per-channel-gate step on a copy of S (V x K); g has K entries."""
+    S = _f64(S).copy()
+    k_raw, v, g = _f64(k_raw), _f64(v), _f64(g)
+    V, K = S.shape
+    _load().kda_step(_ptr(S), V, K, _ptr(k_raw), _ptr(v), _ptr(g), beta, eps)
+    return S
+
+
+def kda_readout(S, q_raw, scale: float = 1.0, eps: float = 1e-6) -> np.ndarray:
+    S, q_raw = _f64(S), _f64(q_raw)
+    V, K = S.shape
+    o = np.empty(V)
+    _load().kda_readout(_ptr(S), V, K, _ptr(q_raw), scale, eps, _ptr(o))
+    return o
+
+
+class OracleKDA:
+    """fp64 state of one KDA layer: checkpoint and a ring whose gate records
+    hold K channels.  A_log [HV], dt_bias [HV, K]; windows carry a [B*T, HV, K].
+    Ring entries start as NaN."""
+
+    def __init__(self, shape, A_log, dt_bias, S0):
+        self.shape = shape
+        self.A_log = _f64(A_log)
+        self.dt_bias = _f64(dt_bias)
+        self.S = _f64(S0).copy()
+        sh = shape
+        self.rawk = np.full((sh.num_slots, sh.H, sh.L, sh.K), np.nan)
+        self.rawv = np.full((sh.num_slots, sh.HV, sh.L, sh.V), np.nan)
+        self.g = np.full((sh.num_slots, sh.HV, sh.L, sh.K), np.nan)
+        self.beta = np.full((sh.num_slots, sh.HV, sh.L), np.nan)
+
+    def _args(self, cur, slot_idx, win=None, o=None, shape=None):
+        sh = shape or self.shape
+        keep = []
+
+        def hold(x):
+            keep.append(x)
+            return x
+
+        A = _KArgs()
+        A.sh = _Shape(sh.B, sh.T, sh.H, sh.HV, sh.K, sh.V, sh.L, sh.max_spec, sh.num_slots,
+                      sh.scale, sh.softplus_threshold, sh.l2norm_eps)
+        A.S, A.rawk, A.rawv = _ptr(self.S), _ptr(self.rawk), _ptr(self.rawv)
+        A.rg, A.rb = _ptr(self.g), _ptr(self.beta)
+        A.wp, A.base, A.flush = _ptr(cur.write_pos, _ip), _ptr(cur.cache_base, _ip), \
+            _ptr(cur.is_flush, _ip)
+        A.slot = _ptr(hold(np.ascontiguousarray(slot_idx, dtype=np.int32)), _ip)
+        if win is not None:
+            A.q, A.k, A.v, A.a, A.b = (_ptr(hold(_f64(x))) for x in win)
+        A.A_log, A.dt_bias = _ptr(self.A_log), _ptr(self.dt_bias)
+        if o is not None:
+            A.o = _ptr(o)
+        return A, keep
+
+    def verify(self, cur, slot_idx, win, write_ring=True, fold_flagged=True, nthreads=None, T=None):
+        """Outputs [B*T, HV, V]; win = (q, k, v, a [B*T,HV,K], b) widened to float64."""
+        sh = self.shape if T is None else self.shape.replace(T=T)
+        sh = sh.replace(B=len(slot_idx))
+        o = np.full((sh.B * sh.T, sh.HV, sh.V), np.nan)
+        A, keep = self._args(cur, slot_idx, win, o=o, shape=sh)
+        A.fold_flagged = int(fold_flagged)
+        _load().kda_verify(ctypes.byref(A), int(write_ring), nthreads or default_threads())
+        del keep
+        return o
+
+    def write_ring(self, cur, slot_idx, win, T=None):
+        sh = self.shape if T is None else self.shape.replace(T=T)
+        sh = sh.replace(B=len(slot_idx))
+        A, keep = self._args(cur, slot_idx, win, shape=sh)
+        _load().kda_write_ring(ctypes.byref(A))
+        del keep
+
+    def fold(self, cur, slot_idx, only_flagged=True, nthreads=None):
+        sh = self.shape.replace(B=len(slot_idx))
+        A, keep = self._args(cur, slot_idx, shape=sh)
+        A.only_flagged = int(only_flagged)
+        _load().kda_fold(ctypes.byref(A), nthreads or default_threads())
+        del keep

@@ -130,3 +130,47 @@ def dcache_window(S0, d_hist, keys, values, g, beta, queries, hist, scale=1.0, e
         wt = np.exp(Gam[i] - Gam[: i + 1]) * (kh[: i + 1] @ qh[t])
         out[t] = scale * (np.exp(Gam[i]) * (S0 @ qh[t]) + wt @ D[: i + 1])
     return out, D_w
+
+
+def kda_window_outputs(S0, keys, values, g, beta, queries, hist, scale=1.0, eps=1e-6):
+    """Outputs [T, V] of the per-channel-gate (KDA) window, in closed form.
+
+    g is [n, K]: record i decays key channel c by e^{g_ic}.  With the prefix
+    sums Gam_i = sum_{m<=i} g_m (vectors over the channels), induction on the
+    step gives
+
+        S_i = S0 diag(e^{Gam_i}) + sum_{j<=i} d_j (kh_j * e^{Gam_i - Gam_j})^T
+
+    and d_i = beta_i (v_i - S_{i-1} diag(e^{g_i}) kh_i) becomes
+
+        (I + A) D = R,  A_ij = beta_i sum_c kh_ic kh_jc e^{Gam_ic - Gam_jc}  (j < i)
+                        R_i  = beta_i (v_i - S0 (e^{Gam_i} * kh_i))
+        o_t = scale (S0 (e^{Gam_i} * qh_t) + sum_{j<=i} (sum_c kh_jc e^{Gam_ic - Gam_jc} qh_tc) d_j),
+        i = hist + t.
+
+    With every channel's gate equal it is ``window_outputs``.  Solved with
+    ``numpy.linalg.solve``.
+    """
+    S0 = np.asarray(S0, dtype=np.float64)
+    kh = normalise(keys, eps)
+    qh = normalise(queries, eps)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    n = kh.shape[0]
+    T = qh.shape[0]
+    Gam = np.cumsum(g, axis=0)                                   # [n, K]
+    A = np.zeros((n, n))
+    for i in range(n):
+        for j in range(i):
+            A[i, j] = beta[i] * np.sum(kh[i] * kh[j] * np.exp(Gam[i] - Gam[j]))
+    R = beta[:, None] * (values - (np.exp(Gam) * kh) @ S0.T)
+    D = np.linalg.solve(np.eye(n) + A, R)
+    out = np.empty((T, S0.shape[0]))
+    for t in range(T):
+        i = hist + t
+        acc = S0 @ (np.exp(Gam[i]) * qh[t])
+        for j in range(i + 1):
+            acc = acc + np.sum(kh[j] * np.exp(Gam[i] - Gam[j]) * qh[t]) * D[j]
+        out[t] = scale * acc
+    return out
