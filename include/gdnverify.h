@@ -222,6 +222,69 @@ int gdn_exact_fold(const gdn_shape *shape, int num_layers,
                    int only_flagged, void *stream);
 
 /*
+ * gdn_kda_spec_verify_ring -- the verify step of one KDA layer, whose gate is
+ * a vector over the key channels (PR #36821 summary: the KDA spec ring keeps
+ * g per record as K fp32 values, ring layout [slots, HV, L, K], beside raw k,
+ * raw v and a scalar beta; the same ring discipline and lifecycle as the GDN
+ * ring).  Same arguments and side effects as gdn_spec_verify_ring, except:
+ *    a         [B*T, HV, K]             (act dtype)   b [B*T, HV] as before
+ *    dt_bias   [HV, K] fp32             A_log [HV] fp32
+ *    ring_g    [num_slots, HV, L, K] fp32
+ * For every non-padding row b with slot s and value head hv:
+ *   g_c = -exp(A_log[hv]) softplus(a[., hv, c] + dt_bias[hv, c]),
+ *   beta = sigmoid(b);
+ *   step: column c of the state decays by e^{g_c}, then the delta rule
+ *   u = S k_hat, S += beta (v - u) k_hat^T;  o_t = scale S_t q_hat_t.
+ *   hist = is_flush[s] ? 0 : write_pos[s]; the outputs come from S[s,hv]
+ *   stepped through hist committed records, then window tokens 0..t.
+ * The verify is one launch that replays the history from the frozen
+ * checkpoint (the per-channel decay has no scalar closed form to regroup):
+ * fold_flagged = 1 makes a flagged row store the state reached after its
+ * write_pos records into S[s] (the exact fold, same records and arithmetic
+ * as gdn_kda_exact_fold) and verify its window from there; fold_flagged = 0
+ * verifies a flagged row from S[s] with an empty history.
+ * write_ring = 1: ring_rawk/ring_rawv receive the k/v bits and
+ *   ring_g[s, hv, p, :] / ring_beta[s, hv, p] the fp32 channel gates and
+ *   beta the kernel used, at p = (cache_base + write_pos + t) & (L-1);
+ *   outputs are bitwise identical with write_ring = 0.
+ * Supported: the gdn_shape envelope with V a multiple of 64 (a workgroup
+ * holds 64 state rows); other shapes return GDN_EUNSUPPORTED.  a and b are
+ * read element by element (no word-pair rule).  ring_g must be 16-byte
+ * aligned.  o must not alias any input.
+ */
+int gdn_kda_spec_verify_ring(const gdn_shape *shape,
+                             const void *q, const void *k, const void *v,
+                             const void *a, const void *b,
+                             const float *A_log, const float *dt_bias,
+                             float *S, const int32_t *slot_idx,
+                             const int32_t *write_pos, const int32_t *cache_base,
+                             const int32_t *is_flush,
+                             void *ring_rawk, void *ring_rawv,
+                             float *ring_g, float *ring_beta,
+                             int write_ring, int fold_flagged,
+                             void *o, void *stream);
+
+/*
+ * gdn_kda_exact_fold -- the exact fold of a KDA layer's committed records
+ * into its checkpoint: gdn_exact_fold's contract (rows, only_flagged, layer
+ * strides, cursors untouched) with the KDA step and ring_g [num_slots, HV,
+ * L, K]; layer l's ring_g starts l * layer_stride_ring * HV * L * K elements
+ * past ring_g.  Bitwise the state a fold_flagged verify stores.
+ * Same support envelope as gdn_kda_spec_verify_ring.
+ */
+int gdn_kda_exact_fold(const gdn_shape *shape, int num_layers,
+                       int64_t layer_stride_S, int64_t layer_stride_ring,
+                       float *S, const void *ring_rawk, const void *ring_rawv,
+                       const float *ring_g, const float *ring_beta,
+                       const int32_t *slot_idx, const int32_t *write_pos,
+                       const int32_t *cache_base, const int32_t *is_flush,
+                       int only_flagged, void *stream);
+
+/* Bytes of one KDA layer's ring: num_slots * L records of raw k, raw v,
+ * K channel gates and beta (0 for an invalid or unsupported shape). */
+size_t gdn_kda_ring_bytes(const gdn_shape *shape);
+
+/*
  * gdn_advance_cursors -- commit by accept count (replayssm(B)SpecDecode §4.2,
  * §8.1-8.2, §9.3).  For each non-padding row with slot s and a = clamp(accept):
  *   if is_flush[s]: cache_base[s] = (cache_base[s] + write_pos[s]) & (L-1);

@@ -9,4 +9,5 @@ from .gdnverify import (  # noqa: F401
     gdn_advance_cursors, gdn_exact_fold, gdn_recurrent_verify_snapshot, gdn_reset_cursors,
     gdn_ring_bytes, gdn_snapshot_bytes, gdn_snapshot_commit, gdn_spec_verify_ring,
     gdn_validate_shape, lib, status_str, gdn_spec_verify_dcache, gdn_dring_bytes,
+    gdn_kda_spec_verify_ring, gdn_kda_exact_fold, gdn_kda_ring_bytes,
 )

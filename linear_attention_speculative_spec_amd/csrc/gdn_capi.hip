@@ -58,6 +58,35 @@ int check_shape(const gdn_shape* sh)
     return GDN_OK;
 }
 
+// Layer count of a multi-layer fold; its work items (row, layer, value head,
+// value tile) are counted in 32-bit ints.
+int check_layers(const gdn_shape& s, int num_layers)
+{
+    if (num_layers < 1)
+        return GDN_EINVAL;
+    if (static_cast<long long>(num_layers) * s.HV > 65535 ||
+        static_cast<long long>(s.B) * num_layers * s.HV * (s.V / 16) > 0x7FFFFFFFLL)
+        return GDN_EUNSUPPORTED;
+    return GDN_OK;
+}
+
+// Layer strides of a multi-layer fold (0: back to back), resolved in place.
+int resolve_layer_strides(const gdn_shape& sh, int num_layers, int64_t& layer_stride_S,
+                          int64_t& layer_stride_ring)
+{
+    const int64_t layer_S = static_cast<int64_t>(sh.num_slots) * sh.HV * sh.V * sh.K;
+    if (layer_stride_S < 0 || layer_stride_ring < 0)
+        return GDN_EINVAL;
+    if (layer_stride_S == 0)
+        layer_stride_S = layer_S;
+    if (layer_stride_ring == 0)
+        layer_stride_ring = sh.num_slots;
+    if (num_layers > 1 &&
+        (layer_stride_S < layer_S || layer_stride_ring < sh.num_slots || layer_stride_S % 4 != 0))
+        return GDN_EINVAL;
+    return GDN_OK;
+}
+
 size_t act_bytes(const gdn_shape& s)
 {
     return s.act == GDN_BF16 ? 2 : 4;
@@ -205,19 +234,13 @@ int gdn_exact_fold(const gdn_shape* shape, int num_layers, int64_t layer_stride_
     if (st != GDN_OK)
         return st;
     const gdn_shape& sh = *shape;
-    if (num_layers < 1 || static_cast<long long>(num_layers) * sh.HV > 65535)
-        return num_layers < 1 ? GDN_EINVAL : GDN_EUNSUPPORTED;
+    st = check_layers(sh, num_layers);
+    if (st != GDN_OK)
+        return st;
     // per-layer strides: fp32 elements of S, slots of the ring arrays
-    const int64_t layer_S = static_cast<int64_t>(sh.num_slots) * sh.HV * sh.V * sh.K;
-    if (layer_stride_S < 0 || layer_stride_ring < 0)
-        return GDN_EINVAL;
-    if (layer_stride_S == 0)
-        layer_stride_S = layer_S;
-    if (layer_stride_ring == 0)
-        layer_stride_ring = sh.num_slots;
-    if (num_layers > 1 &&
-        (layer_stride_S < layer_S || layer_stride_ring < sh.num_slots || layer_stride_S % 4 != 0))
-        return GDN_EINVAL;
+    st = resolve_layer_strides(sh, num_layers, layer_stride_S, layer_stride_ring);
+    if (st != GDN_OK)
+        return st;
     if (!ok_ptr(S, 16) || !ok_ptr(ring_rawk, 16) || !ok_ptr(ring_rawv, 16) || !ok_ptr(ring_g, 4) ||
         !ok_ptr(ring_beta, 4) || !ok_ptr(slot_idx, 4) || !ok_ptr(write_pos, 4) ||
         !ok_ptr(cache_base, 4) || (only_flagged && !ok_ptr(is_flush, 4)))
@@ -227,6 +250,77 @@ int gdn_exact_fold(const gdn_shape* shape, int num_layers, int64_t layer_stride_
     const CursorPtrs c = {write_pos, cache_base, is_flush};
     return status_of(launch_fold(sh, num_layers, layer_stride_S, layer_stride_ring, S, r, slot_idx,
                                  c, only_flagged ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_kda_spec_verify_ring(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                             const void* a, const void* b, const float* A_log, const float* dt_bias,
+                             float* S, const int32_t* slot_idx, const int32_t* write_pos,
+                             const int32_t* cache_base, const int32_t* is_flush, void* ring_rawk,
+                             void* ring_rawv, float* ring_g, float* ring_beta, int write_ring,
+                             int fold_flagged, void* o, void* stream)
+{
+    int st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape& sh = *shape;
+    if (!kda_shape_supported(sh))
+        return GDN_EUNSUPPORTED;
+    const size_t eb = act_bytes(sh);
+    if (!ok_ptr(q, 16) || !ok_ptr(k, 16) || !ok_ptr(v, 16) || !ok_ptr(a, eb) || !ok_ptr(b, eb) ||
+        !ok_ptr(A_log, 4) || !ok_ptr(dt_bias, 4) || !ok_ptr(S, 16) || !ok_ptr(slot_idx, 4) ||
+        !ok_ptr(write_pos, 4) || !ok_ptr(cache_base, 4) || !ok_ptr(is_flush, 4) ||
+        !ok_ptr(ring_rawk, 16) || !ok_ptr(ring_rawv, 16) || !ok_ptr(ring_g, 16) ||
+        !ok_ptr(ring_beta, 4) || !ok_ptr(o, 16))
+        return GDN_EINVAL;
+    if (o == q || o == k || o == v || o == S)
+        return GDN_EINVAL;
+    const WindowPtrs w = {q, k, v, a, b, A_log, dt_bias};
+    const CursorPtrs c = {write_pos, cache_base, is_flush};
+    const RingPtrs r = {ring_rawk, ring_rawv, ring_g, ring_beta};
+    // one launch: history replay (stored for flagged rows), then the window
+    return status_of(launch_kda_verify(sh, w, S, slot_idx, c, r, write_ring ? 1 : 0,
+                                       fold_flagged ? 1 : 0, o, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_kda_exact_fold(const gdn_shape* shape, int num_layers, int64_t layer_stride_S,
+                       int64_t layer_stride_ring, float* S, const void* ring_rawk,
+                       const void* ring_rawv, const float* ring_g, const float* ring_beta,
+                       const int32_t* slot_idx, const int32_t* write_pos, const int32_t* cache_base,
+                       const int32_t* is_flush, int only_flagged, void* stream)
+{
+    int st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape& sh = *shape;
+    if (!kda_shape_supported(sh))
+        return GDN_EUNSUPPORTED;
+    st = check_layers(sh, num_layers);
+    if (st != GDN_OK)
+        return st;
+    st = resolve_layer_strides(sh, num_layers, layer_stride_S, layer_stride_ring);
+    if (st != GDN_OK)
+        return st;
+    if (!ok_ptr(S, 16) || !ok_ptr(ring_rawk, 16) || !ok_ptr(ring_rawv, 16) || !ok_ptr(ring_g, 16) ||
+        !ok_ptr(ring_beta, 4) || !ok_ptr(slot_idx, 4) || !ok_ptr(write_pos, 4) ||
+        !ok_ptr(cache_base, 4) || (only_flagged && !ok_ptr(is_flush, 4)))
+        return GDN_EINVAL;
+    const RingPtrs r = {const_cast<void*>(ring_rawk), const_cast<void*>(ring_rawv),
+                        const_cast<float*>(ring_g), const_cast<float*>(ring_beta)};
+    const CursorPtrs c = {write_pos, cache_base, is_flush};
+    return status_of(launch_kda_fold(sh, num_layers, layer_stride_S, layer_stride_ring, S, r,
+                                     slot_idx, c, only_flagged ? 1 : 0,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_kda_ring_bytes(const gdn_shape* shape)
+{
+    if (check_shape(shape) != GDN_OK || !kda_shape_supported(*shape))
+        return 0;
+    const gdn_shape& s = *shape;
+    const size_t eb = act_bytes(s);
+    const size_t rec = static_cast<size_t>(s.H) * s.K * eb + static_cast<size_t>(s.HV) * s.V * eb +
+                       static_cast<size_t>(s.HV) * s.K * 4 + static_cast<size_t>(s.HV) * 4;
+    return static_cast<size_t>(s.num_slots) * s.L * rec;
 }
 
 int gdn_advance_cursors(const gdn_shape* shape, const int32_t* slot_idx, const int32_t* accept,

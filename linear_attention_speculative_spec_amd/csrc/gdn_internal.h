@@ -56,6 +56,19 @@ hipError_t launch_fold(const gdn_shape& sh, int num_layers, int64_t layer_stride
                        const int32_t* slot_idx, const CursorPtrs& c, int only_flagged,
                        hipStream_t stream);
 
+// The per-channel-gate (KDA) layer: ring g [num_slots, HV, L, K], window a
+// [B*T, HV, K], dt_bias [HV, K].  Verify by replay from the checkpoint (a
+// flagged row folds when fold_flagged), and the multi-layer exact fold.
+bool kda_shape_supported(const gdn_shape& sh);
+
+hipError_t launch_kda_verify(const gdn_shape& sh, const WindowPtrs& w, float* S, const int32_t* slot_idx,
+                             const CursorPtrs& c, const RingPtrs& r, int write_ring, int fold_flagged, void* o,
+                             hipStream_t stream);
+
+hipError_t launch_kda_fold(const gdn_shape& sh, int num_layers, int64_t layer_stride_S, int64_t layer_stride_ring,
+                           float* S, const RingPtrs& r, const int32_t* slot_idx, const CursorPtrs& c,
+                           int only_flagged, hipStream_t stream);
+
 hipError_t launch_snapshot(const gdn_shape& sh, const WindowPtrs& w, const float* S,
                            const int32_t* slot_idx, float* snap, void* o, const RingPtrs& r,
                            const int32_t* write_pos, const int32_t* cache_base, int write_ring,

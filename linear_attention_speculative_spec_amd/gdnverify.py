@@ -23,6 +23,7 @@ EXPORTED = (
     "gdn_recurrent_verify_snapshot", "gdn_snapshot_commit", "gdn_ring_bytes",
     "gdn_snapshot_bytes", "gdn_validate_shape", "gdn_status_str",
     "gdn_spec_verify_dcache", "gdn_dring_bytes",
+    "gdn_kda_spec_verify_ring", "gdn_kda_exact_fold", "gdn_kda_ring_bytes",
 )
 
 
@@ -70,13 +71,15 @@ def lib():
         L.gdn_spec_verify_ring.argtypes = [_sp] + [_vp] * 16 + [_i, _i, _vp, _vp]
         L.gdn_spec_verify_dcache.argtypes = [_sp] + [_vp] * 17 + [_i, _i, _vp, _vp]
         L.gdn_exact_fold.argtypes = [_sp, _i, ctypes.c_int64, ctypes.c_int64] + [_vp] * 9 + [_i, _vp]
+        L.gdn_kda_spec_verify_ring.argtypes = [_sp] + [_vp] * 16 + [_i, _i, _vp, _vp]
+        L.gdn_kda_exact_fold.argtypes = [_sp, _i, ctypes.c_int64, ctypes.c_int64] + [_vp] * 9 + [_i, _vp]
         L.gdn_advance_cursors.argtypes = [_sp] + [_vp] * 6
         L.gdn_reset_cursors.argtypes = [_sp, _vp, ctypes.c_int32, ctypes.c_int32] + [_vp] * 4
         L.gdn_recurrent_verify_snapshot.argtypes = [_sp] + [_vp] * 17 + [_i, _vp]
         L.gdn_snapshot_commit.argtypes = [_sp] + [_vp] * 5
         for fn in ("gdn_spec_verify_ring", "gdn_spec_verify_dcache", "gdn_exact_fold", "gdn_advance_cursors",
                    "gdn_reset_cursors", "gdn_recurrent_verify_snapshot", "gdn_snapshot_commit",
-                   "gdn_validate_shape"):
+                   "gdn_validate_shape", "gdn_kda_spec_verify_ring", "gdn_kda_exact_fold"):
             getattr(L, fn).restype = ctypes.c_int
         L.gdn_validate_shape.argtypes = [_sp]
         L.gdn_ring_bytes.argtypes = [_sp]
@@ -85,6 +88,8 @@ def lib():
         L.gdn_snapshot_bytes.restype = ctypes.c_size_t
         L.gdn_dring_bytes.argtypes = [_sp]
         L.gdn_dring_bytes.restype = ctypes.c_size_t
+        L.gdn_kda_ring_bytes.argtypes = [_sp]
+        L.gdn_kda_ring_bytes.restype = ctypes.c_size_t
         L.gdn_status_str.argtypes = [_i]
         L.gdn_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -155,6 +160,27 @@ def _ring_checks(sh, rawk, rawv, g, beta, layers=1, slot_stride=0):
     _need("ring_beta", beta, slots * sh.HV * sh.L, torch.float32)
 
 
+def _kda_window_checks(sh, q, k, v, a, b, A_log, dt_bias):
+    act = _act_dtype(sh)
+    n = sh.B * sh.T
+    _need("q", q, n * sh.H * sh.K, act)
+    _need("k", k, n * sh.H * sh.K, act)
+    _need("v", v, n * sh.HV * sh.V, act)
+    _need("a", a, n * sh.HV * sh.K, act)
+    _need("b", b, n * sh.HV, act)
+    _need("A_log", A_log, sh.HV, torch.float32)
+    _need("dt_bias", dt_bias, sh.HV * sh.K, torch.float32)
+
+
+def _kda_ring_checks(sh, rawk, rawv, g, beta, layers=1, slot_stride=0):
+    act = _act_dtype(sh)
+    slots = (layers - 1) * (slot_stride or sh.num_slots) + sh.num_slots
+    _need("ring_rawk", rawk, slots * sh.H * sh.L * sh.K, act)
+    _need("ring_rawv", rawv, slots * sh.HV * sh.L * sh.V, act)
+    _need("ring_g", g, slots * sh.HV * sh.L * sh.K, torch.float32)
+    _need("ring_beta", beta, slots * sh.HV * sh.L, torch.float32)
+
+
 def _cursor_checks(sh, *cur):
     for name, c in zip(("write_pos", "cache_base", "is_flush"), cur):
         _need(name, c, sh.num_slots, torch.int32)
@@ -203,13 +229,51 @@ def gdn_exact_fold(shape, num_layers, layer_stride_S, layer_stride_ring, S, ring
     _ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta, layers=num_layers,
                  slot_stride=layer_stride_ring)
     _need("slot_idx", slot_idx, shape.B, torch.int32)
-    _cursor_checks(shape, write_pos, cache_base, is_flush)
+    _cursor_checks(shape, write_pos, cache_base, *((is_flush,) if only_flagged else ()))
     st = lib().gdn_exact_fold(ctypes.byref(shape), int(num_layers), int(layer_stride_S),
                               int(layer_stride_ring), _ptr(S), _ptr(ring_rawk),
                               _ptr(ring_rawv), _ptr(ring_g), _ptr(ring_beta), _ptr(slot_idx),
                               _ptr(write_pos), _ptr(cache_base), _ptr(is_flush),
                               int(only_flagged), _stream(stream))
     _check("gdn_exact_fold", st)
+
+
+def gdn_kda_spec_verify_ring(shape, q, k, v, a, b, A_log, dt_bias, S, slot_idx, write_pos,
+                             cache_base, is_flush, ring_rawk, ring_rawv, ring_g, ring_beta,
+                             write_ring, fold_flagged, o, stream=None):
+    _kda_window_checks(shape, q, k, v, a, b, A_log, dt_bias)
+    _need("S", S, shape.num_slots * shape.HV * shape.V * shape.K, torch.float32)
+    _need("slot_idx", slot_idx, shape.B, torch.int32)
+    _cursor_checks(shape, write_pos, cache_base, is_flush)
+    _kda_ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta)
+    _need("o", o, shape.B * shape.T * shape.HV * shape.V, _act_dtype(shape))
+    st = lib().gdn_kda_spec_verify_ring(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+        _ptr(dt_bias), _ptr(S), _ptr(slot_idx), _ptr(write_pos), _ptr(cache_base),
+        _ptr(is_flush), _ptr(ring_rawk), _ptr(ring_rawv), _ptr(ring_g), _ptr(ring_beta),
+        int(write_ring), int(fold_flagged), _ptr(o), _stream(stream))
+    _check("gdn_kda_spec_verify_ring", st)
+
+
+def gdn_kda_exact_fold(shape, num_layers, layer_stride_S, layer_stride_ring, S, ring_rawk,
+                       ring_rawv, ring_g, ring_beta, slot_idx, write_pos, cache_base, is_flush,
+                       only_flagged, stream=None):
+    per_layer = shape.num_slots * shape.HV * shape.V * shape.K
+    _need("S", S, (num_layers - 1) * (layer_stride_S or per_layer) + per_layer, torch.float32)
+    _kda_ring_checks(shape, ring_rawk, ring_rawv, ring_g, ring_beta, layers=num_layers,
+                     slot_stride=layer_stride_ring)
+    _need("slot_idx", slot_idx, shape.B, torch.int32)
+    _cursor_checks(shape, write_pos, cache_base, *((is_flush,) if only_flagged else ()))
+    st = lib().gdn_kda_exact_fold(ctypes.byref(shape), int(num_layers), int(layer_stride_S),
+                                  int(layer_stride_ring), _ptr(S), _ptr(ring_rawk),
+                                  _ptr(ring_rawv), _ptr(ring_g), _ptr(ring_beta), _ptr(slot_idx),
+                                  _ptr(write_pos), _ptr(cache_base), _ptr(is_flush),
+                                  int(only_flagged), _stream(stream))
+    _check("gdn_kda_exact_fold", st)
+
+
+def gdn_kda_ring_bytes(shape) -> int:
+    return int(lib().gdn_kda_ring_bytes(ctypes.byref(shape)))
 
 
 def gdn_advance_cursors(shape, slot_idx, accept, write_pos, cache_base, is_flush, stream=None):

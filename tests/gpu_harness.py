@@ -190,3 +190,88 @@ class Pair:
         T = self.shape.T
         idx = (self.orows[:, None] * T + np.arange(T)[None, :]).reshape(-1)
         return host_f64(o)[idx]
+
+
+# ------------------------------------------------- per-channel-gate (KDA) layer
+
+class KdaGpuLayer(GpuLayer):
+    """One KDA layer's device tensors: dt_bias [HV, K], ring g [slots, HV, L, K]."""
+
+    def verify(self, cur, slot_idx, win: DevWindow, o, write_ring=1, fold_flagged=1, gs=None):
+        gv.gdn_kda_spec_verify_ring(gs or self.gs, win.q, win.k, win.v, win.a, win.b, self.A_log,
+                                    self.dt_bias, self.S, slot_idx, cur[0], cur[1], cur[2],
+                                    self.rawk, self.rawv, self.g, self.beta, write_ring,
+                                    fold_flagged, o)
+
+    def fold(self, cur, slot_idx, only_flagged=1, gs=None):
+        gv.gdn_kda_exact_fold(gs or self.gs, 1, 0, 0, self.S, self.rawk, self.rawv, self.g,
+                              self.beta, slot_idx, cur[0], cur[1], cur[2], only_flagged)
+
+
+class KdaPair:
+    """A GPU KDA layer and an oracle KDA layer from one seed, rings pre-filled
+    (GPU: the library's verify with one-token windows, write_ring on, no fold;
+    oracle: its own ring write of the same raw records)."""
+
+    def __init__(self, shape: synth.LayerShape, seed: int, variant: str = "base",
+                 wp_by_slot=None, base_by_slot=None, slots=None, oracle_rows=None):
+        require_gpu()
+        self.shape = shape
+        self.act = shape.act
+        rng = synth.make_rng(seed)
+        self.rng = rng
+        self.variant = variant
+        self.params = synth.kda_layer_params(rng, shape, variant)
+        self.slots = synth.slot_choice(rng, shape) if slots is None else np.asarray(slots, np.int32)
+        cd = synth.random_cursors(rng, shape)
+        wp = cd.write_pos if wp_by_slot is None else np.asarray(wp_by_slot, np.int32)
+        base = cd.cache_base if base_by_slot is None else np.asarray(base_by_slot, np.int32)
+        self.template = synth.kda_ring_garbage_template(rng, shape)
+        self.gpu = KdaGpuLayer(shape, self.params, self.template)
+        self.orows = np.arange(shape.B) if oracle_rows is None else np.asarray(oracle_rows)
+        osh = shape.replace(B=len(self.orows), num_slots=len(self.orows))
+        self.oshape = osh
+        self.oslots = np.arange(len(self.orows), dtype=np.int32)
+        gslots = self.slots[self.orows]
+        self.gslots = gslots
+        self.orc = oracle.OracleKDA(osh, self.params.A_log, self.params.dt_bias,
+                                    self.params.S0[gslots])
+        nrec = int(wp[self.slots].max()) if len(self.slots) else 0
+        hist = synth.kda_history_windows(rng, shape, nrec, variant)
+        gs1 = self.gpu.gs.replace(T=1)
+        cur_g = CursorState(np.zeros(shape.num_slots, np.int32), base.copy(),
+                            np.zeros(shape.num_slots, np.int32))
+        cur_o = CursorState(np.zeros(osh.num_slots, np.int32), base[gslots].copy(),
+                            np.zeros(osh.num_slots, np.int32))
+        scratch = self.gpu.new_out(T=1)
+        for r, (sl, w) in enumerate(zip(helpers.prefill_plan(self.slots, wp, nrec), hist)):
+            cur_g.write_pos[:] = r
+            self.gpu.verify(dev_cursors(cur_g), dev_i32(sl), DevWindow(w, self.act), scratch,
+                            write_ring=1, fold_flagged=0, gs=gs1)
+            cur_o.write_pos[:] = r
+            osl = np.where(sl[self.orows] >= 0, self.oslots, -1).astype(np.int32)
+            wo = helpers.window_rows(w, self.orows, 1)
+            self.orc.write_ring(cur_o, osl, helpers.win_f64(wo, self.act), T=1)
+        torch.cuda.synchronize()
+        self.cur = CursorState(wp.copy(), base.copy(),
+                               (wp + 2 * shape.max_spec > shape.L).astype(np.int32))
+        self.ocur = CursorState(wp[gslots].copy(), base[gslots].copy(),
+                                self.cur.is_flush[gslots].copy())
+        self.dcur = dev_cursors(self.cur)
+        self.dslots = dev_i32(self.slots)
+        self.hist = hist
+        self.wp0 = wp.copy()
+        self.base0 = base.copy()
+
+    def window(self) -> synth.Window:
+        return synth.kda_window(self.rng, self.shape, self.variant)
+
+    def oracle_verify(self, win: synth.Window, write_ring=True, fold_flagged=True):
+        wo = helpers.window_rows(win, self.orows, self.shape.T)
+        return self.orc.verify(self.ocur, self.oslots, helpers.win_f64(wo, self.act),
+                               write_ring=write_ring, fold_flagged=fold_flagged)
+
+    def gpu_out_rows(self, o: torch.Tensor) -> np.ndarray:
+        T = self.shape.T
+        idx = (self.orows[:, None] * T + np.arange(T)[None, :]).reshape(-1)
+        return host_f64(o)[idx]

@@ -77,6 +77,9 @@ def test_invalid_shapes_are_rejected(override, status):
     assert L.gdn_reset_cursors(ctypes.byref(sh), n, 0, 0, n, n, n, n) == status
     assert L.gdn_recurrent_verify_snapshot(ctypes.byref(sh), *([n] * 17), 0, n) == status
     assert L.gdn_snapshot_commit(ctypes.byref(sh), *([n] * 5)) == status
+    assert L.gdn_kda_spec_verify_ring(ctypes.byref(sh), *([n] * 16), 1, 1, n, n) == status
+    assert L.gdn_kda_exact_fold(ctypes.byref(sh), 1, 0, 0, *([n] * 9), 1, n) == status
+    assert gv.gdn_kda_ring_bytes(sh) == 0
 
 
 def test_null_and_misaligned_pointers_are_rejected():
@@ -157,3 +160,47 @@ def test_bf16_gate_words_stay_inside_the_buffers():
     # fp32 activations read a and b element by element: an odd count is fine
     odd32 = odd.replace(act=gv.GDN_F32)
     assert gv.gdn_validate_shape(odd32) == gv.GDN_OK
+
+
+def test_kda_envelope_pointers_and_footprint():
+    # the per-channel-gate layer: 64-row state tiles (V a multiple of 64),
+    # 16-byte aligned ring_g, is_flush required by the fold only with
+    # only_flagged; refused on the host before any launch
+    L = gv.lib()
+    n = None
+    base = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"])
+    args = [ctypes.c_void_p((3 + i) << 20) for i in range(16)]
+    out = ctypes.c_void_p(40 << 20)
+    v48 = base.replace(V=48)
+    assert gv.gdn_validate_shape(v48) == gv.GDN_OK
+    assert L.gdn_kda_spec_verify_ring(ctypes.byref(v48), *args, 1, 1, out, n) == gv.GDN_EUNSUPPORTED
+    assert L.gdn_kda_exact_fold(ctypes.byref(v48), 1, 0, 0, *args[:9], 1, n) == gv.GDN_EUNSUPPORTED
+    assert gv.gdn_kda_ring_bytes(v48) == 0
+    mis = list(args)
+    mis[14] = ctypes.c_void_p((17 << 20) + 4)    # ring_g: 4-byte aligned only
+    assert L.gdn_kda_spec_verify_ring(ctypes.byref(base), *mis, 1, 1, out, n) == gv.GDN_EINVAL
+    fold = [ctypes.c_void_p((3 + i) << 20) for i in range(9)]
+    fold[3] = ctypes.c_void_p((6 << 20) + 4)     # ring_g of the fold
+    assert L.gdn_kda_exact_fold(ctypes.byref(base), 1, 0, 0, *fold, 1, n) == gv.GDN_EINVAL
+    fold = [ctypes.c_void_p((3 + i) << 20) for i in range(8)] + [n]   # no is_flush
+    assert L.gdn_kda_exact_fold(ctypes.byref(base), 1, 0, 0, *fold, 1, n) == gv.GDN_EINVAL
+    # output aliasing an input; negative and overlapping layer strides
+    assert L.gdn_kda_spec_verify_ring(ctypes.byref(base), *args, 1, 1, args[0], n) == gv.GDN_EINVAL
+    per_S = base.num_slots * base.HV * base.V * base.K
+    fold = [ctypes.c_void_p((3 + i) << 20) for i in range(9)]
+    for nl, ls, lr in ((2, -4, 0), (3, per_S - 4, 0), (3, 0, base.num_slots - 1), (0, 0, 0)):
+        assert L.gdn_kda_exact_fold(ctypes.byref(base), nl, ls, lr, *fold, 1, n) == gv.GDN_EINVAL
+    # per slot-record: raw k per qk head, raw v, K fp32 gates and a beta per value head
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b256"])
+    rec = 16 * 128 * 2 + 32 * (128 * 2 + 128 * 4 + 4)
+    assert gv.gdn_kda_ring_bytes(sh) == 512 * 64 * rec
+
+
+def test_fold_work_item_count_fits_32_bits():
+    # rows x layers x value heads x 16-row tiles is counted in 32-bit ints
+    L = gv.lib()
+    n = None
+    sh = gv.GdnShape.from_layer(synth.CONFIGS["qwen3next_b32"], B=65535, num_slots=65535)
+    fold = [ctypes.c_void_p((3 + i) << 20) for i in range(9)]
+    for fn in (L.gdn_exact_fold, L.gdn_kda_exact_fold):
+        assert fn(ctypes.byref(sh), 2047, 0, 0, *fold, 1, n) == gv.GDN_EUNSUPPORTED
