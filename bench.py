@@ -11,7 +11,10 @@ and the cursor advance by synthetic accept counts U{0..T}.
 
 Prints one JSON line: draft tokens/s per layer, the verify kernel's achieved
 HBM GB/s against the 8 TB/s peak (algorithmic bytes / event-timed duration),
-the snapshot baseline for comparison and the fp64 CPU oracle's rate.
+the snapshot baseline, the fold-every-commit and d-cache designs for
+comparison, the per-channel-gate (KDA) layer on the same workload (bound by
+the fp32 vector ALU), the 48-layer B=128 stack's whole-step latency and
+memory, and the fp64 CPU oracle's rate at B=256 and B=32.
 """
 from __future__ import annotations
 
@@ -52,6 +55,10 @@ def parse():
                     help="skip the comparison with the d-cache verify")
     ap.add_argument("--no-fold-every-commit", action="store_true",
                     help="skip the comparison with the fold-every-commit design")
+    ap.add_argument("--no-kda", action="store_true",
+                    help="skip the per-channel-gate (KDA) layer leg")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the 48-layer whole-stack leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -110,6 +117,35 @@ def snapshot_alg_bytes(sh) -> int:
     B, T = sh.B, sh.T
     return (B * sh.HV * sh.V * sh.K * 4 + B * T * sh.HV * sh.V * sh.K * 4 +
             B * T * (2 * sh.H * sh.K + sh.HV * sh.V + 2 * sh.HV) * eb + B * T * sh.HV * sh.V * eb)
+
+
+def kda_record_bytes(sh) -> int:
+    eb = 2 if sh.act == "bf16" else 4
+    return sh.H * sh.K * eb + sh.HV * (sh.V * eb + sh.K * 4 + 4)
+
+
+def kda_alg(sh, replayed: int, flagged: int):
+    """(flops, bytes) one KDA verify launch must do and move.
+
+    Flops: a state-row step is a decay multiply, a dot and an update over K
+    columns (5K flops; an FMA counts 2), for every replayed record and window
+    token of every (row, value head, value row); the readout adds 2K per
+    window token.  Bytes: checkpoints read (and written for flagged rows),
+    replayed records, window in, outputs, the window's ring records."""
+    eb = 2 if sh.act == "bf16" else 4
+    B, T = sh.B, sh.T
+    rows = sh.HV * sh.V
+    flops = (replayed + B * T) * rows * 5 * sh.K + B * T * rows * 2 * sh.K
+    state = sh.HV * sh.V * sh.K * 4
+    byts = (B * state + flagged * state + replayed * kda_record_bytes(sh) +
+            B * T * (2 * sh.H * sh.K + sh.HV * sh.V + sh.HV * sh.K + sh.HV) * eb +
+            B * T * sh.HV * sh.V * eb + B * T * kda_record_bytes(sh) + B * 16)
+    return flops, byts
+
+
+# fp32 vector rate without packed fp32 instructions (which this library does not
+# emit): 256 CUs x 4 SIMDs x 16 lanes x 1 FMA (2 flops) per clock x 2.4 GHz
+ALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
 def traffic_from_profile():
@@ -442,10 +478,202 @@ def main():
             f"({dbytes / (d_ver * 1e-6) / 1e9:.0f} GB/s)")
         del rkd, rvd, rgd, rbd, rdd, Sd
 
+    if not args.no_kda:
+        traj = [int(hist_per_step[i].sum() + fold_per_step[i].sum()) for i in range(n_steps)]
+        nflag = [len(fold_per_step[i]) for i in range(n_steps)]
+        result["kda"] = kda_leg(args, sh, saved[0], params.A_log, slots, cd, acc_d, traj, nflag)
+        del saved
+    if not args.no_chain:
+        del S, rawk, rawv, rg, rb
+        torch.cuda.empty_cache()
+        result["chain"] = chain_leg(args)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, args.seed, args.cpu_seconds)
+        b32 = synth.CONFIGS["qwen3next_b32"]
+        result["cpu_baseline"]["qwen3next_b32"] = cpu_baseline(b32, args.seed, args.cpu_seconds / 3)
 
     print(json.dumps(result), flush=True)
+
+
+def kda_leg(args, sh, S0, A_log_h, slots, cd, acc_d, traj, nflag):
+    """The per-channel-gate (KDA) layer on the same workload: same slots,
+    initial cursors and accept counts (so the same history lengths), a
+    checkpoint copied from the GDN leg's, K gate values per record.  A step is
+    the one verify launch (flagged rows fold on the way) plus the cursor
+    advance."""
+    import torch
+
+    from linear_attention_speculative_spec_amd import gdnverify as gv
+    from linear_attention_speculative_spec_amd import synth
+
+    dev = "cuda:0"
+    gs = gv.GdnShape.from_layer(sh)
+    t0 = time.time()
+    rng = synth.make_rng(args.seed + 2)
+    dt_bias = torch.from_numpy(rng.normal(0.0, 0.1, (sh.HV, sh.K)).astype(np.float32)).to(dev)
+    A_log = torch.from_numpy(np.ascontiguousarray(A_log_h, np.float32)).to(dev)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)    # noqa: E731
+    S = S0.clone()
+    rawk = torch.zeros(sh.num_slots, sh.H, sh.L, sh.K, dtype=torch.bfloat16, device=dev)
+    rawv = torch.zeros(sh.num_slots, sh.HV, sh.L, sh.V, dtype=torch.bfloat16, device=dev)
+    rg = torch.zeros(sh.num_slots, sh.HV, sh.L, sh.K, dtype=torch.float32, device=dev)
+    rb = torch.zeros(sh.num_slots, sh.HV, sh.L, dtype=torch.float32, device=dev)
+    dslots = i32(slots)
+    dw = synth.DeviceWindows(args.seed + 2, sh, kda=True)
+    pool = [dw.draw() for _ in range(4)]
+    dw1 = synth.DeviceWindows(args.seed + 3, sh.replace(T=1), kda=True)
+    gs1 = gs.replace(T=1)
+    scratch = torch.empty(sh.B, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    zeros, base_d = i32(np.zeros(sh.num_slots)), i32(cd.cache_base)
+    n_hist = int(cd.write_pos[slots].max())
+    for r in range(n_hist):
+        w = dw1.draw()
+        sl = np.where(cd.write_pos[slots] > r, slots, -1).astype(np.int32)
+        gv.gdn_kda_spec_verify_ring(gs1, w["q"], w["k"], w["v"], w["a"], w["b"], A_log, dt_bias,
+                                    S, i32(sl), i32(np.full(sh.num_slots, r)), base_d, zeros,
+                                    rawk, rawv, rg, rb, 1, 0, scratch)
+    wp0 = cd.write_pos.astype(np.int32)
+    cur = [i32(wp0), i32(cd.cache_base), i32((wp0 + 2 * sh.max_spec > sh.L).astype(np.int32))]
+    o = torch.empty(sh.B * sh.T, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] kda: rings pre-filled with up to {n_hist} records ({time.time() - t0:.1f}s)")
+
+    def step(i, ev=None):
+        w = pool[i % len(pool)]
+        if ev is not None:
+            ev[0].record()
+        gv.gdn_kda_spec_verify_ring(gs, w["q"], w["k"], w["v"], w["a"], w["b"], A_log, dt_bias,
+                                    S, dslots, *cur, rawk, rawv, rg, rb, 1, 1, o)
+        if ev is not None:
+            ev[1].record()
+        gv.gdn_advance_cursors(gs, dslots, acc_d[i], *cur)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / args.steps * 1e3
+    ver = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    timed = range(args.warmup, args.warmup + args.steps)
+    fl, by = np.mean([kda_alg(sh, traj[i], nflag[i]) for i in timed], axis=0)
+    v_us = float(ver.mean())
+    tflops = fl / (v_us * 1e-6) / 1e12
+    log(f"[bench] kda: step {step_us:.1f} us, verify {v_us:.1f} us ({tflops:.1f} TFLOP/s fp32)")
+    return {
+        "step_us": step_us,
+        "draft_tokens_per_s": sh.B * sh.T / (step_us * 1e-6),
+        "roofline": {"bound": "alu", "kernel": "kda_kernel (verify)", "achieved": tflops,
+                     "peak": ALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / ALU_F32_PEAK_TFLOPS, "traffic": None,
+                     "alg_flops_per_launch": float(fl), "alg_bytes_per_launch": float(by),
+                     "achieved_GBs": by / (v_us * 1e-6) / 1e9, "avg_launch_us": v_us},
+        "replayed_records_per_step": float(np.mean([traj[i] for i in timed])),
+        "ring_bytes_per_layer": gv.gdn_kda_ring_bytes(gs),
+        "snapshot_bytes_per_layer": gv.gdn_snapshot_bytes(gs)}
+
+
+def chain_leg(args):
+    """The 48-layer stack of Qwen3-Next-shaped GDN layers at B=128 (T=4,
+    L=64, 256 slots): one whole-stack verify step is the all-layer fold of the
+    flagged rows (one launch), then the 48 layers' ring verifies, then one
+    cursor advance.  Each layer reads a pre-drawn window (the glue between
+    layers is not part of the path); its own checkpoint and ring."""
+    import torch
+
+    from linear_attention_speculative_spec_amd import gdnverify as gv
+    from linear_attention_speculative_spec_amd import synth
+
+    dev = "cuda:0"
+    sh = synth.CONFIGS["layer_chain_b128"]
+    NL = 48
+    gs = gv.GdnShape.from_layer(sh)
+    t0 = time.time()
+    dw = synth.DeviceWindows(args.seed + 10, sh)
+    gen = dw.gen
+    A_log = torch.log(torch.rand((NL, sh.HV), generator=gen, device=dev) * 15.0 + 1.0)
+    dt_bias = torch.randn((NL, sh.HV), generator=gen, device=dev) * 0.1
+    S = torch.empty((NL, sh.num_slots, sh.HV, sh.V, sh.K), dtype=torch.float32, device=dev)
+    for l in range(NL):
+        S[l].normal_(0.0, 0.02, generator=gen)
+    rawk = torch.zeros((NL, sh.num_slots, sh.H, sh.L, sh.K), dtype=torch.bfloat16, device=dev)
+    rawv = torch.zeros((NL, sh.num_slots, sh.HV, sh.L, sh.V), dtype=torch.bfloat16, device=dev)
+    rg = torch.zeros((NL, sh.num_slots, sh.HV, sh.L), dtype=torch.float32, device=dev)
+    rb = torch.zeros_like(rg)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)    # noqa: E731
+    rng = synth.make_rng(args.seed + 10)
+    slots = synth.slot_choice(rng, sh)
+    cd = synth.random_cursors(rng, sh)
+    dslots = i32(slots)
+    gs1 = gs.replace(T=1)
+    dw1 = synth.DeviceWindows(args.seed + 11, sh.replace(T=1))
+    scratch = torch.empty((sh.B, sh.HV, sh.V), dtype=torch.bfloat16, device=dev)
+    zeros, base_d = i32(np.zeros(sh.num_slots)), i32(cd.cache_base)
+    n_hist = int(cd.write_pos[slots].max())
+    for r in range(n_hist):
+        sl = i32(np.where(cd.write_pos[slots] > r, slots, -1))
+        wp_r = i32(np.full(sh.num_slots, r))
+        w = dw1.draw()
+        for l in range(NL):
+            gv.gdn_spec_verify_ring(gs1, w["q"], w["k"], w["v"], w["a"], w["b"], A_log[l],
+                                    dt_bias[l], S[l], sl, wp_r, base_d, zeros, rawk[l], rawv[l],
+                                    rg[l], rb[l], 1, 0, scratch)
+    wp0 = cd.write_pos.astype(np.int32)
+    cur = [i32(wp0), i32(cd.cache_base), i32((wp0 + 2 * sh.max_spec > sh.L).astype(np.int32))]
+    pool = [dw.draw() for _ in range(4)]
+    o = torch.empty((sh.B * sh.T, sh.HV, sh.V), dtype=torch.bfloat16, device=dev)
+    warm, steps = 3, 10
+    accepts = [i32(a) for a in synth.accept_counts(rng, sh.B, sh.T, warm + steps)]
+    torch.cuda.synchronize()
+    log(f"[bench] chain: {NL} layers pre-filled with up to {n_hist} records "
+        f"({time.time() - t0:.1f}s)")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        gv.gdn_exact_fold(gs, NL, 0, 0, S, rawk, rawv, rg, rb, dslots, *cur, 1)
+        if ev is not None:
+            ev[1].record()
+        for l in range(NL):
+            w = pool[(i + l) % len(pool)]
+            gv.gdn_spec_verify_ring(gs, w["q"], w["k"], w["v"], w["a"], w["b"], A_log[l],
+                                    dt_bias[l], S[l], dslots, *cur, rawk[l], rawv[l], rg[l], rb[l],
+                                    1, 0, o)
+        if ev is not None:
+            ev[2].record()
+        gv.gdn_advance_cursors(gs, dslots, accepts[i], *cur)
+
+    for i in range(warm):
+        step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for j in range(steps):
+        step(warm + j, evs[j])
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    fold_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+    ver_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3)
+    log(f"[bench] chain: step {step_ms:.3f} ms (fold {fold_us:.1f} us, {NL} verifies "
+        f"{ver_us:.1f} us)")
+    return {
+        "workload": f"{NL} GDN layers, B={sh.B}, {sh.num_slots} slots, H={sh.H}, HV={sh.HV}, "
+                    f"K=V={sh.K}, T={sh.T}, L={sh.L}, bf16 act, fp32 state",
+        "step_ms": step_ms,
+        "all_layer_fold_us": fold_us,
+        "verify_us_per_layer": ver_us / NL,
+        "draft_tokens_per_s": sh.B * sh.T / (step_ms * 1e-3),
+        "ring_bytes_stack": NL * gv.gdn_ring_bytes(gs),
+        "snapshot_bytes_stack": NL * gv.gdn_snapshot_bytes(gs),
+        "checkpoint_bytes_stack": NL * sh.num_slots * sh.HV * sh.V * sh.K * 4}
 
 
 COPY_BYTES = 256 << 20
@@ -613,7 +841,12 @@ def cpu_baseline(sh, seed, budget_s):
         orc.verify(cur, oslots, w64, write_ring=False, fold_flagged=False, nthreads=nt)
         t_used += time.perf_counter() - t1
         reps += 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": reps * sh.B * sh.T / t_used, "unit": "draft tokens/s", "cores": nt,
+            "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
             "kind": "oracle",
             "sample": f"{reps} full verifies of the B={sh.B} batch (all {sh.HV} value heads, "
                       f"history replay + {sh.T} drafts, fp64), {t_used:.1f} s wall on {nt} threads"}

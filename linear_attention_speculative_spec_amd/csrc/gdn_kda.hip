@@ -236,10 +236,19 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
     };
 
     const int nbatch = (n + RB - 1) / RB;
-    if (nbatch > 0) {
+    if (nbatch > 0)
         issue(0);
+    // The state rows' loads complete here on every path (a use of each row
+    // register), so that the record loop below carries no wait for them: a
+    // wait placed there would also hold up, at the first record of every
+    // batch, the prefetch of the next batch issued after the state's loads.
+#pragma unroll
+    for (int r = 0; r < kKdaRPG; ++r)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            asm volatile("" ::"v"(sv[r][e]));
+    if (nbatch > 0)
         commit(0, min(RB, n));
-    }
     __syncthreads();
     for (int bi = 0; bi < nbatch; ++bi) {
         const int buf = bi & 1;

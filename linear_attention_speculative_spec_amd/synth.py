@@ -268,11 +268,12 @@ class DeviceWindows:
     """
 
     def __init__(self, seed: int, shape: LayerShape, variant: str = "base",
-                 device: str = "cuda:0"):
+                 device: str = "cuda:0", kda: bool = False):
         import torch
 
         self.torch = torch
         self.shape = shape
+        self.kda = kda          # per-channel gate inputs: a is [n, HV, K]
         self.variant = variant
         self.device = device
         self.gen = torch.Generator(device=device)
@@ -291,7 +292,8 @@ class DeviceWindows:
         n = sh.B * sh.T if n_tok is None else n_tok
         bmean = 4.0 if self.variant == "beta_high" else 0.0
         return {"q": self.normal((n, sh.H, sh.K)), "k": self.normal((n, sh.H, sh.K)),
-                "v": self.normal((n, sh.HV, sh.V)), "a": self.normal((n, sh.HV)),
+                "v": self.normal((n, sh.HV, sh.V)),
+                "a": self.normal((n, sh.HV, sh.K) if self.kda else (n, sh.HV)),
                 "b": self.normal((n, sh.HV), bmean)}
 
     def host_rows(self, win: dict, rows, T: int) -> Window:
