@@ -4,9 +4,10 @@
 //
 // A KDA layer's gate is a vector over the key channels: the ring keeps K fp32
 // gate values per record beside raw k, raw v and a scalar beta (PR #36821
-// summary: g [slots, HV, L, K] fp32, "per-K KDA gate"; the same ring
-// discipline and verify -> commit -> verify lifecycle as the GDN ring).  The
-// step decays state column c by e^{g_c}:
+// summary, the KDA spec ring layout checked by _replayssm_ring_ok: g is
+// [slots, HV, L, K] fp32; the same ring discipline and verify -> commit ->
+// verify lifecycle as the GDN ring).  The step decays state column c by
+// e^{g_c}:
 //     S[:, c] <- e^{g_c} S[:, c];  u = S k_hat;  S <- S + beta (v - u) k_hat^T
 // and o_t = scale S_t q_hat_t.  g_c = -exp(A_log) softplus(a_c + dt_bias_c),
 // the GDN gate per channel.
@@ -14,13 +15,13 @@
 // Execution: a persistent grid over items (row, value head, tile of 64
 // value rows); a workgroup of 4 waves holds the tile's state rows in
 // registers, four rows per 16-lane group (lane c holds columns 64 m + 4 c ..
-// +3 of each), and steps them through the records: the committed history
-// (staged through LDS in double-buffered batches of 16: normalised keys,
-// channel decays, values, betas), then the draft window with its outputs.
-// A row flagged for flush stores the state reached after its history (the
-// exact fold) and verifies its window from there.  The work is the
-// sequential recurrence: this kernel is bound by the fp32 vector ALU, not
-// by HBM.
+// +3 of each), and steps them through the records: the committed history,
+// staged through LDS in batches of 16 (the next batch's loads in flight
+// while the current one is stepped) and stepped two records at a time, then
+// the draft window with its outputs.  A row flagged for flush stores the
+// state reached after its history (the exact fold) and verifies its window
+// from there.  The work is the sequential recurrence: this kernel is bound
+// by the fp32 vector ALU, not by HBM.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -51,14 +52,31 @@ constexpr int kKdaThreads = 256;
 constexpr int kKdaBatch = 16;   // records per LDS batch (and window tokens at most)
 constexpr int kKdaRPG = 4;      // state rows per 16-lane group
 
+// Records are replayed in pairs: two steps j, j+1 from state S are
+//     u_j     = S . (d_j * kh_j)
+//     u_j+1   = S . (d_j * d_j+1 * kh_j+1) + delta_j c_j,   c_j = kh_j . (d_j+1 * kh_j+1)
+//     S      <- S * (d_j * d_j+1) + delta_j (kh_j * d_j+1)^T + delta_j+1 kh_j+1^T
+// with d the channel decays e^{g} and delta = beta (v - u): the state takes
+// one multiply and two FMAs per element for two records instead of two of
+// each, and the two dots are independent.  Only products of decays appear,
+// so nothing can overflow.  The five vectors and c_j of a pair are formed
+// once per batch, shared by every state row.
 template <class Act, int K>
 struct KdaShared {
     static constexpr int TR = 16 * kKdaRPG;                 // tile rows
     static constexpr int VU = TR * Act::bytes / 16;         // 16-byte units of a record's tile values
-    uint4 vbuf[2][kKdaBatch * VU];                          // tile values per record
-    float bbuf[2][kKdaBatch];                               // beta
-    float khs[2][kKdaBatch][K];                             // normalised keys (window: keys, queries)
-    float dks[2][kKdaBatch][K];                             // channel decays e^{g_c}
+    static constexpr int NP = kKdaBatch / 2;                // record pairs per batch
+    uint4 vbuf[kKdaBatch * VU];                             // tile values per record
+    float bbuf[kKdaBatch];                                  // beta
+    float cbuf[NP];                                         // c_j of each pair
+    // per pair: d_j kh_j, d_j d_j+1 kh_j+1, d_j d_j+1, kh_j d_j+1, kh_j+1 (rows
+    // 5 pp .. 5 pp + 4).  The window reuses the space: 16 rows each of keys,
+    // queries and decays.
+    float rows[48][K];
+    __device__ float* pair_vec(int pp, int i) { return rows[5 * pp + i]; }
+    __device__ float* win_key(int t) { return rows[t]; }
+    __device__ float* win_query(int t) { return rows[16 + t]; }
+    __device__ float* win_decay(int t) { return rows[32 + t]; }
 };
 
 template <int EPL>
@@ -153,41 +171,31 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
     const float* rg = p.rg + (recs * p.HV + (static_cast<size_t>(s) * p.HV + hv) * L) * K;
     const float* rb = p.rb + recs * p.HV + (static_cast<size_t>(s) * p.HV + hv) * L;
 
-    // one batch in flight: the key columns this thread normalises (record
-    // row16 of the batch), a chunk of tile values, 8 gate values and a beta
+    // one batch in flight: lane c of group row16 holds record row16 of the
+    // batch at columns 64 m + 4 c .. +3 (raw key and gate); a chunk of tile
+    // values and a beta
     typedef typename std::conditional<Act::bytes == 4, uint4, uint2>::type KRaw;
-    constexpr int GPT = (RB * K) / kKdaThreads;             // gate values per thread per batch (4, 8 or 16)
-    static_assert(GPT % 4 == 0, "gate chunk");
     KRaw kreg[K / 64];
+    f32x4 greg[K / 64];
     uint4 vreg;
-    f32x4 greg[GPT / 4];
     float breg;
     auto issue = [&](int bi) {
         const int jk = bi * RB + row16;
+        const size_t roff = static_cast<size_t>((base + jk) & (L - 1)) * K + 4 * c;
 #pragma unroll
         for (int m = 0; m < K / 64; ++m) {
             kreg[m] = KRaw{};
-            if (jk < n)
-                kreg[m] = *reinterpret_cast<const KRaw*>(rk + static_cast<size_t>((base + jk) & (L - 1)) * K +
-                                                         64 * m + 4 * c);
+            greg[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (jk < n) {
+                kreg[m] = *reinterpret_cast<const KRaw*>(rk + roff + 64 * m);
+                greg[m] = *reinterpret_cast<const f32x4*>(rg + roff + 64 * m);
+            }
         }
         vreg = uint4{0u, 0u, 0u, 0u};
         if (tid < RB * VU) {
             const int j = bi * RB + tid / VU;
             if (j < n)
                 vreg = reinterpret_cast<const uint4*>(rv + static_cast<size_t>((base + j) & (L - 1)) * p.V)[tid % VU];
-        }
-        // gate values: thread tid holds channels (tid * GPT) % K .. + GPT of record (tid * GPT) / K
-        {
-            const int j = bi * RB + (tid * GPT) / K;
-            const int c0 = (tid * GPT) % K;
-#pragma unroll
-            for (int q4 = 0; q4 < GPT / 4; ++q4) {
-                greg[q4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                if (j < n)
-                    greg[q4] = *reinterpret_cast<const f32x4*>(rg + static_cast<size_t>((base + j) & (L - 1)) * K +
-                                                                c0 + 4 * q4);
-            }
         }
         breg = 0.0f;
         if (tid < RB) {
@@ -196,23 +204,14 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
                 breg = rb[(base + j) & (L - 1)];
         }
     };
-    auto commit = [&](int buf, int cnt) {
+    // Records past the batch's count act as identity steps: key 0, decay 1,
+    // beta 0 and value 0 (so an odd count ends with a half-empty pair).
+    auto commit = [&](int cnt) {
         if (tid < RB * VU)
-            sh.vbuf[buf][tid] = vreg;
-        {
-            const int jj = (tid * GPT) / K;
-            const int c0 = (tid * GPT) % K;
-#pragma unroll
-            for (int q4 = 0; q4 < GPT / 4; ++q4) {
-                const f32x4 gv = greg[q4];
-                *reinterpret_cast<f32x4*>(&sh.dks[buf][jj][c0 + 4 * q4]) =
-                    f32x4{expf(gv[0]), expf(gv[1]), expf(gv[2]), expf(gv[3])};
-            }
-        }
+            sh.vbuf[tid] = vreg;
         if (tid < RB)
-            sh.bbuf[buf][tid] = breg;
-        // keys: 16 lane groups normalise the batch's records in parallel
-        float kc[EPL], kh[EPL];
+            sh.bbuf[tid] = breg;
+        float kc[EPL], kh[EPL], dk[EPL];
 #pragma unroll
         for (int m = 0; m < K / 64; ++m) {
             f32x4 t;
@@ -222,16 +221,49 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             else
                 t = f32x4{__uint_as_float(kreg[m].x << 16), __uint_as_float(kreg[m].x & 0xFFFF0000u),
                           __uint_as_float(kreg[m].y << 16), __uint_as_float(kreg[m].y & 0xFFFF0000u)};
+            const f32x4 gv = greg[m];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e) {
                 kc[4 * m + e] = t[e];
+                dk[4 * m + e] = expf(gv[e]);     // gate 0 past the count: decay 1
+            }
         }
-        if (row16 < cnt) {
-            const float r = kda_rnorm16<EPL>(kc, p.eps);
+        const bool live = row16 < cnt;
+        const float r = kda_rnorm16<EPL>(kc, p.eps);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                kh[e] = kc[e] * r;
-            put_cols_f32<K>(sh.khs[buf][row16], c, kh);
+        for (int e = 0; e < EPL; ++e)
+            kh[e] = live ? kc[e] * r : 0.0f;
+        // the partner record (row16 ^ 1) sits in the paired 16-lane row
+        float kp[EPL], dp[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            kp[e] = __shfl_xor(kh[e], 16, 64);
+            dp[e] = __shfl_xor(dk[e], 16, 64);
+        }
+        const int pp = row16 >> 1;
+        float x0[EPL], x1[EPL], x2[EPL];
+        if ((row16 & 1) == 0) {        // record j: d_j kh_j, d_j d_j+1 kh_j+1, d_j d_j+1
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                x2[e] = dk[e] * dp[e];
+                x0[e] = dk[e] * kh[e];
+                x1[e] = x2[e] * kp[e];
+            }
+            put_cols_f32<K>(sh.pair_vec(pp, 0), c, x0);
+            put_cols_f32<K>(sh.pair_vec(pp, 1), c, x1);
+            put_cols_f32<K>(sh.pair_vec(pp, 2), c, x2);
+        } else {                       // record j+1: kh_j d_j+1, kh_j+1 and c_j
+            float cp = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                x0[e] = kp[e] * dk[e];
+                cp = __builtin_fmaf(x0[e], kh[e], cp);
+            }
+            cp = group16_sum(cp);
+            put_cols_f32<K>(sh.pair_vec(pp, 3), c, x0);
+            put_cols_f32<K>(sh.pair_vec(pp, 4), c, kh);
+            if (c == 0)
+                sh.cbuf[pp] = cp;
         }
     };
 
@@ -248,27 +280,57 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
         for (int e = 0; e < EPL; ++e)
             asm volatile("" ::"v"(sv[r][e]));
     if (nbatch > 0)
-        commit(0, min(RB, n));
+        commit(min(RB, n));
     __syncthreads();
+    // one LDS buffer: the next batch is committed after a barrier that ends
+    // every thread's reads of the current one (its loads were in flight
+    // meanwhile)
     for (int bi = 0; bi < nbatch; ++bi) {
-        const int buf = bi & 1;
         if (bi + 1 < nbatch)
             issue(bi + 1);
         const int cnt = min(RB, n - bi * RB);
-        const st* vb = reinterpret_cast<const st*>(sh.vbuf[buf]);
-        for (int jj = 0; jj < cnt; ++jj) {
-            float kh[EPL], dk[EPL];
-            cols_f32<K>(sh.khs[buf][jj], c, kh);
-            cols_f32<K>(sh.dks[buf][jj], c, dk);
-            const float bta = sh.bbuf[buf][jj];
+        const st* vb = reinterpret_cast<const st*>(sh.vbuf);
+        for (int pp = 0; pp < (cnt + 1) >> 1; ++pp) {
+            float a0[EPL], a1[EPL];
+            cols_f32<K>(sh.pair_vec(pp, 0), c, a0);
+            cols_f32<K>(sh.pair_vec(pp, 1), c, a1);
+            const float cj = sh.cbuf[pp];
+            const float b0 = sh.bbuf[2 * pp], b1 = sh.bbuf[2 * pp + 1];
+            float d0[kKdaRPG], d1[kKdaRPG];
 #pragma unroll
-            for (int r = 0; r < kKdaRPG; ++r)
-                kda_step_row<EPL>(sv[r], kh, dk, Act::load(vb + jj * TR + 16 * r + row16), bta);
+            for (int r = 0; r < kKdaRPG; ++r) {
+                float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    u0 = __builtin_fmaf(sv[r][e], a0[e], u0);
+                    u1 = __builtin_fmaf(sv[r][e], a1[e], u1);
+                }
+                u0 = group16_sum(u0);
+                u1 = group16_sum(u1);
+                const float v0 = Act::load(vb + (2 * pp) * TR + 16 * r + row16);
+                const float v1 = Act::load(vb + (2 * pp + 1) * TR + 16 * r + row16);
+                d0[r] = b0 * (v0 - u0);
+                u1 = __builtin_fmaf(d0[r], cj, u1);
+                d1[r] = b1 * (v1 - u1);
+            }
+            float dd[EPL], kd[EPL], k1[EPL];
+            cols_f32<K>(sh.pair_vec(pp, 2), c, dd);
+            cols_f32<K>(sh.pair_vec(pp, 3), c, kd);
+            cols_f32<K>(sh.pair_vec(pp, 4), c, k1);
+#pragma unroll
+            for (int r = 0; r < kKdaRPG; ++r) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    float x = sv[r][e] * dd[e];
+                    x = __builtin_fmaf(d0[r], kd[e], x);
+                    sv[r][e] = __builtin_fmaf(d1[r], k1[e], x);
+                }
+            }
         }
-        // the other buffer was last read by the previous batch, which every
-        // thread finished before the barrier that ended it
-        if (bi + 1 < nbatch)
-            commit(buf ^ 1, min(RB, n - (bi + 1) * RB));
+        if (bi + 1 < nbatch) {
+            __syncthreads();
+            commit(min(RB, n - (bi + 1) * RB));
+        }
         __syncthreads();
     }
 }
@@ -291,7 +353,7 @@ __device__ void kda_window(P& p, KdaShared<Act, K>& sh, int b, int s, int wpc, i
     const int T = p.T, L = p.L;
     const size_t tok0 = static_cast<size_t>(b) * T;
     const bool ring = p.write_ring != 0;
-    st* vb = reinterpret_cast<st*>(sh.vbuf[0]);
+    st* vb = reinterpret_cast<st*>(sh.vbuf);
 
     // keys and queries: one token per 16-lane group
     if (row16 < T) {
@@ -304,13 +366,13 @@ __device__ void kda_window(P& p, KdaShared<Act, K>& sh, int b, int s, int wpc, i
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             xh[e] = xc[e] * r;
-        put_cols_f32<K>(sh.khs[0][t], c, xh);
+        put_cols_f32<K>(sh.win_key(t), c, xh);
         act_cols<Act, K>(qr, c, xc);
         r = kda_rnorm16<EPL>(xc, p.eps);
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             xh[e] = xc[e] * r;
-        put_cols_f32<K>(sh.khs[1][t], c, xh);
+        put_cols_f32<K>(sh.win_query(t), c, xh);
         if (ring && hv % G == 0 && tile == 0) {
             const int ph = (base + wpc + t) & (L - 1);
             st* dk = static_cast<st*>(p.rawk) + ((static_cast<size_t>(s) * p.H + h) * L + ph) * K;
@@ -334,7 +396,7 @@ __device__ void kda_window(P& p, KdaShared<Act, K>& sh, int b, int s, int wpc, i
         const int t = e / K, ch = e % K;
         const float g = kda_gate_c(Act::load(static_cast<const st*>(p.a) + ((tok0 + t) * p.HV + hv) * K + ch),
                                    p.dt_bias[static_cast<size_t>(hv) * K + ch], A_log, p.softplus_threshold);
-        sh.dks[0][t][ch] = expf(g);
+        sh.win_decay(t)[ch] = expf(g);
         if (ring && tile == 0)
             p.rg[((static_cast<size_t>(s) * p.HV + hv) * L + ((base + wpc + t) & (L - 1))) * K + ch] = g;
     }
@@ -342,7 +404,7 @@ __device__ void kda_window(P& p, KdaShared<Act, K>& sh, int b, int s, int wpc, i
         const int t = tid;
         const float bv = Act::load(static_cast<const st*>(p.b) + (tok0 + t) * p.HV + hv);
         const float beta = 1.0f / (1.0f + expf(-bv));
-        sh.bbuf[0][t] = beta;
+        sh.bbuf[t] = beta;
         if (ring && tile == 0)
             p.rb[(static_cast<size_t>(s) * p.HV + hv) * L + ((base + wpc + t) & (L - 1))] = beta;
     }
@@ -350,15 +412,15 @@ __device__ void kda_window(P& p, KdaShared<Act, K>& sh, int b, int s, int wpc, i
     for (int t = 0; t < T; ++t) {
         {
             float kh[EPL], dk[EPL];
-            cols_f32<K>(sh.khs[0][t], c, kh);
-            cols_f32<K>(sh.dks[0][t], c, dk);
-            const float bta = sh.bbuf[0][t];
+            cols_f32<K>(sh.win_key(t), c, kh);
+            cols_f32<K>(sh.win_decay(t), c, dk);
+            const float bta = sh.bbuf[t];
 #pragma unroll
             for (int r = 0; r < kKdaRPG; ++r)
                 kda_step_row<EPL>(sv[r], kh, dk, Act::load(vb + t * TR + 16 * r + row16), bta);
         }
         float qh[EPL];
-        cols_f32<K>(sh.khs[1][t], c, qh);
+        cols_f32<K>(sh.win_query(t), c, qh);
 #pragma unroll
         for (int r = 0; r < kKdaRPG; ++r) {
             float dot = 0.0f;
@@ -390,7 +452,7 @@ __device__ __forceinline__ KKda* launder_kda(KKda* pk)
 }
 
 template <class Act, int K, bool kVerify>
-__global__ __launch_bounds__(kKdaThreads) void kda_kernel(const KdaParams p_arg, int num_layers)
+__global__ __launch_bounds__(kKdaThreads, K <= 128 ? 4 : 2) void kda_kernel(const KdaParams p_arg, int num_layers)
 {
     (void)p_arg;   // read through the argument segment instead
     KKda* pk = launder_kda((KKda*)__builtin_amdgcn_kernarg_segment_ptr());
