@@ -130,6 +130,12 @@ typedef struct gdn_shape {
  * activations, so for act = GDN_BF16 they must be 4-byte aligned
  * (GDN_EINVAL otherwise) and B*T*HV must be even (GDN_EUNSUPPORTED
  * otherwise), so that no word reaches past the last element.
+ * fp32 activations: the key-side products run on bf16 matrix units, so fp32
+ * keys and queries enter them as a bf16 high part plus a bf16 remainder
+ * (about 16 significant bits; the remainder-by-remainder product is
+ * dropped).  Everything else (norms, gates, the solve, the checkpoint
+ * products, the state and the outputs) is fp32.  The outputs stay within
+ * 1e-5 of the fp64 recurrence on the fp32 workloads, far inside 2e-3.
  */
 int gdn_spec_verify_ring(const gdn_shape *shape,
                          const void *q, const void *k, const void *v,

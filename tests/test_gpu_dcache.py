@@ -76,7 +76,7 @@ def run_dcache_lifecycle(shape, seed, steps, variant="base", wp_by_slot=None, or
         if i % 4 == 3 or i == steps - 1:
             worst["d"] = max(worst["d"], check_d_ring(P, tr, tol))
     tr.check(P.gpu, P.orc, gslots)
-    say(f"d-cache lifecycle {shape.act} B={shape.B} T={shape.T} K={shape.K} V={shape.V} "
+    helpers.report(f"d-cache lifecycle {shape.act} B={shape.B} T={shape.T} K={shape.K} V={shape.V} "
         f"L={shape.L} {variant}: steps={steps} flushes={flushes} "
         + " ".join(f"max_rel({k})={v:.2e}" for k, v in worst.items()))
     return P, flushes

@@ -174,8 +174,9 @@ def run_lifecycle(shape, seed, steps, variant="base", wp_by_slot=None, oracle_ro
         assert serr <= tol, (i, serr)
     if tr is not None:
         tr.check(P.gpu, P.orc, gslots)
-    say(f"lifecycle {shape.act} B={shape.B} T={shape.T} L={shape.L} {variant}: "
-        f"steps={steps} flushes={flushes} max_rel(o)={worst_o:.2e} max_rel(S)={worst_s:.2e}")
+    helpers.report(f"lifecycle {shape.act} B={shape.B} T={shape.T} K={shape.K} V={shape.V} L={shape.L} "
+                   f"{variant}: steps={steps} flushes={flushes} max_rel(o)={worst_o:.2e} "
+                   f"max_rel(S)={worst_s:.2e}")
     return P, flushes
 
 
