@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain device copy of COPY_BYTES "
                          "(the reference for scaling the HBM byte counters)")
+    ap.add_argument("--summarize-kda-profile", metavar="DIR",
+                    help="no GPU work: write the KDA kernel's profile summary from the rocprofv3 "
+                         "CSVs under DIR/kt and DIR/alu")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="no GPU work: write the profile summary from the rocprofv3 CSVs "
                          "under DIR/kt, DIR/fetch and DIR/write")
@@ -176,6 +179,9 @@ def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
+        return
+    if args.summarize_kda_profile:
+        summarize_kda_profile(args.summarize_kda_profile)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -797,6 +803,90 @@ def summarize_profile(d):
     path = PROFILE_SUMMARY
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+KDA_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "kda_kernel_qwen3next_b256.md")
+KDA_SRC = os.path.join(ROOT, "linear_attention_speculative_spec_amd", "csrc", "gdn_kda.hip")
+KDA_PROFILE_CMDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/kprof/kt -o run --output-format csv -- "
+    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "--no-dcache --no-chain > $R/gpurun_out/kprof/kt.log 2>&1",
+    "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+    "SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE -d $R/gpurun_out/kprof/alu -o run --output-format csv -- "
+    "python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
+    "--no-dcache --no-chain",
+    "cd $R && python3 bench.py --summarize-kda-profile gpurun_out/kprof",
+]
+
+
+def summarize_kda_profile(d):
+    """Profile summary (markdown) of the KDA verify kernel: its average
+    duration over the timed steps of the KDA leg, and its instruction
+    counters against the fp32 vector issue rate."""
+    steps_kt, steps_pmc = 20, 3
+    is_ver = lambda name: "kda_kernel" in name and ("true" in name or "Lb1E" in name)   # noqa: E731
+    trace = _csv(os.path.join(d, "kt", "run_kernel_trace.csv"))
+    stats = _csv(os.path.join(d, "kt", "run_kernel_stats.csv"))
+    ver = [r for r in trace if is_ver(r["Kernel_Name"])]
+    timed = ver[-steps_kt:]
+    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed]) * 1e-3
+    kname = timed[-1]["Kernel_Name"]
+    flops = None
+    try:
+        for line in open(os.path.join(d, "kt.log")):
+            if line.startswith("{"):
+                flops = json.loads(line)["kda"]["roofline"]["alg_flops_per_launch"]
+    except (OSError, KeyError):
+        pass
+    rows = _csv(os.path.join(d, "alu", "run_counter_collection.csv"))
+
+    def cval(name):
+        v = [float(r["Counter_Value"]) for r in rows
+             if r["Counter_Name"] == name and is_ver(r["Kernel_Name"])][-steps_pmc:]
+        return float(np.mean(v)) if v else float("nan")
+
+    valu, lds, salu = cval("SQ_INSTS_VALU"), cval("SQ_INSTS_LDS"), cval("SQ_INSTS_SALU")
+    waves, gui = cval("SQ_WAVES"), cval("GRBM_GUI_ACTIVE")
+    t = dur.mean() * 1e-6
+    clock = gui / XCDS / t
+    issue = valu * 4 / SIMDS / clock            # a wave's VALU instruction takes 4 cycles of its SIMD
+    src_hash = hashlib.sha256(open(KDA_SRC, "rb").read()).hexdigest()[:16]
+    out = ["# kda_kernel (verify), KDA layer B=256 (qwen3next_b256 workload shape)\n",
+           "Commands (from the repository root on the GPU host, `R=$PWD`; each profiler run under "
+           "its own `timeout`):\n",
+           "```\n" + "\n".join(KDA_PROFILE_CMDS) + "\n```\n",
+           f"- kernel source: `linear_attention_speculative_spec_amd/csrc/gdn_kda.hip`, "
+           f"source sha256[:16]: `{src_hash}`",
+           f"- dispatch: `{kname}`",
+           f"- timed steps (last {steps_kt} KDA verify dispatches of the kernel-trace run): "
+           f"average {dur.mean():.1f} us, min {dur.min():.1f} us, max {dur.max():.1f} us\n",
+           "## --kernel-trace --stats (all dispatches of the run)\n",
+           "| kernel | calls | average us | total ms | % |", "|---|---|---|---|---|"]
+    for r in stats[:8]:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) * 1e-3:.1f} | "
+                   f"{float(r['TotalDurationNs']) * 1e-6:.2f} | {float(r['Percentage']):.1f} |")
+    out.append("\nThe KDA kernel's stats line also averages the ring pre-fill calls (one-token windows); "
+               "the timed-step average above is the figure bench.py's HIP events report.\n")
+    out.append(f"## Instructions per launch (--pmc, mean of the last {steps_pmc} KDA verify dispatches)\n")
+    out.append("| SQ_INSTS_VALU | SQ_INSTS_LDS | SQ_INSTS_SALU | SQ_WAVES | GRBM_GUI_ACTIVE |")
+    out.append("|---|---|---|---|---|")
+    out.append(f"| {valu:.4e} | {lds:.4e} | {salu:.4e} | {waves:.0f} | {gui:.4e} |")
+    out.append(f"\nClock over the timed average: GRBM_GUI_ACTIVE / {XCDS} dies / {dur.mean():.1f} us = "
+               f"{clock / 1e9:.2f} GHz.")
+    out.append(f"VALU issue time: SQ_INSTS_VALU x 4 cycles / {SIMDS} SIMDs / clock = {issue * 1e6:.1f} us, "
+               f"{100.0 * issue / t:.0f}% of the kernel's time (100% would mean every SIMD issues a "
+               f"vector instruction every 4 cycles).")
+    if flops:
+        out.append(f"\nAlgorithmic flops per launch (bench.py accounting): {flops:.4e}; "
+                   f"{flops / t / 1e12:.1f} TFLOP/s at the timed average, "
+                   f"{flops / t / 1e12 / ALU_F32_PEAK_TFLOPS:.3f} of the non-packed fp32 peak "
+                   f"({ALU_F32_PEAK_TFLOPS:.1f} TFLOP/s at 2.4 GHz); "
+                   f"{flops / valu:.1f} flops per wave-level VALU instruction (at most 128).")
+    os.makedirs(os.path.dirname(KDA_PROFILE_SUMMARY), exist_ok=True)
+    with open(KDA_PROFILE_SUMMARY, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
