@@ -66,7 +66,8 @@ struct KdaShared {
     static constexpr int TR = 16 * kKdaRPG;                 // tile rows
     static constexpr int VU = TR * Act::bytes / 16;         // 16-byte units of a record's tile values
     static constexpr int NP = kKdaBatch / 2;                // record pairs per batch
-    uint4 vbuf[kKdaBatch * VU];                             // tile values per record
+    uint4 vbuf[kKdaBatch * VU];                             // window: tile values per token
+    float bvf[kKdaBatch * TR];                              // replay: beta v per record and tile row
     float bbuf[kKdaBatch];                                  // beta
     float cbuf[NP];                                         // c_j of each pair
     // per pair: d_j kh_j, d_j d_j+1 kh_j+1, d_j d_j+1, kh_j d_j+1, kh_j+1 (rows
@@ -178,7 +179,7 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
     KRaw kreg[K / 64];
     f32x4 greg[K / 64];
     uint4 vreg;
-    float breg;
+    float breg, bvreg;
     auto issue = [&](int bi) {
         const int jk = bi * RB + row16;
         const size_t roff = static_cast<size_t>((base + jk) & (L - 1)) * K + 4 * c;
@@ -192,10 +193,14 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             }
         }
         vreg = uint4{0u, 0u, 0u, 0u};
+        bvreg = 0.0f;
         if (tid < RB * VU) {
             const int j = bi * RB + tid / VU;
-            if (j < n)
-                vreg = reinterpret_cast<const uint4*>(rv + static_cast<size_t>((base + j) & (L - 1)) * p.V)[tid % VU];
+            if (j < n) {
+                const int ph = (base + j) & (L - 1);
+                vreg = reinterpret_cast<const uint4*>(rv + static_cast<size_t>(ph) * p.V)[tid % VU];
+                bvreg = rb[ph];                  // the record's beta, for beta v
+            }
         }
         breg = 0.0f;
         if (tid < RB) {
@@ -207,8 +212,23 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
     // Records past the batch's count act as identity steps: key 0, decay 1,
     // beta 0 and value 0 (so an odd count ends with a half-empty pair).
     auto commit = [&](int cnt) {
-        if (tid < RB * VU)
-            sh.vbuf[tid] = vreg;
+        if (tid < RB * VU) {
+            // beta v in fp32: the step then forms delta = beta v - beta u in one FMA
+            constexpr int EPC = 16 / Act::bytes;
+            f32x4 w[EPC / 4];
+            if constexpr (Act::bytes == 4) {
+                w[0] = f32x4{__uint_as_float(vreg.x), __uint_as_float(vreg.y), __uint_as_float(vreg.z),
+                             __uint_as_float(vreg.w)};
+            } else {
+                w[0] = f32x4{__uint_as_float(vreg.x << 16), __uint_as_float(vreg.x & 0xFFFF0000u),
+                             __uint_as_float(vreg.y << 16), __uint_as_float(vreg.y & 0xFFFF0000u)};
+                w[1] = f32x4{__uint_as_float(vreg.z << 16), __uint_as_float(vreg.z & 0xFFFF0000u),
+                             __uint_as_float(vreg.w << 16), __uint_as_float(vreg.w & 0xFFFF0000u)};
+            }
+#pragma unroll
+            for (int h4 = 0; h4 < EPC / 4; ++h4)
+                *reinterpret_cast<f32x4*>(&sh.bvf[(tid / VU) * TR + (tid % VU) * EPC + 4 * h4]) = w[h4] * bvreg;
+        }
         if (tid < RB)
             sh.bbuf[tid] = breg;
         float kc[EPL], kh[EPL], dk[EPL];
@@ -289,7 +309,6 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
         if (bi + 1 < nbatch)
             issue(bi + 1);
         const int cnt = min(RB, n - bi * RB);
-        const st* vb = reinterpret_cast<const st*>(sh.vbuf);
         for (int pp = 0; pp < (cnt + 1) >> 1; ++pp) {
             float a0[EPL], a1[EPL];
             cols_f32<K>(sh.pair_vec(pp, 0), c, a0);
@@ -307,11 +326,11 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
                 }
                 u0 = group16_sum(u0);
                 u1 = group16_sum(u1);
-                const float v0 = Act::load(vb + (2 * pp) * TR + 16 * r + row16);
-                const float v1 = Act::load(vb + (2 * pp + 1) * TR + 16 * r + row16);
-                d0[r] = b0 * (v0 - u0);
+                const float bv0 = sh.bvf[(2 * pp) * TR + 16 * r + row16];
+                const float bv1 = sh.bvf[(2 * pp + 1) * TR + 16 * r + row16];
+                d0[r] = __builtin_fmaf(-b0, u0, bv0);
                 u1 = __builtin_fmaf(d0[r], cj, u1);
-                d1[r] = b1 * (v1 - u1);
+                d1[r] = __builtin_fmaf(-b1, u1, bv1);
             }
             float dd[EPL], kd[EPL], k1[EPL];
             cols_f32<K>(sh.pair_vec(pp, 2), c, dd);
