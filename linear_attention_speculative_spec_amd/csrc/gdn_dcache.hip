@@ -22,20 +22,34 @@
 // logical positions write_pos + t beside the raw records, for the verifies
 // that follow; the exact fold still replays the raw records.
 //
-// Execution: one workgroup (8 waves) per item (row, value head, value tile of
-// up to 128 rows, 16 per wave):
-//   1. the wave's checkpoint rows are issued as 128-bit loads (lane l: row
-//      l % 8 (+8), key columns 32 i + 4 (l / 8)); the window's keys and queries
-//      are normalised into LDS; the gates of the combined sequence are staged;
-//   2. one wave forms the prefix sums of the gates; every thread forms dot
-//      products of the history keys with the window columns; each wave forms
-//      S0 [kh_w, qh_w] for its rows on MFMA 4x4x1 (sums over the eight key
-//      groups by a rotate and lane swaps);
-//   3. the dot products become the coupling (A) and output (F) coefficients;
-//   4. four thread groups split the history, each value row summing its
-//      stored deltas against the coefficients;
-//   5. one thread per value row runs the window's T-step recurrence for its
-//      deltas and forms the outputs; the others write the raw records.
+// Execution: one workgroup of four waves per item (row, value head, up to 64
+// value rows); wave w owns key tile w (records 16 w .. 16 w + 15, and 16 w +
+// 64 .. for 128-record rings) and value tile w (rows 16 w .. 16 w + 15):
+//   1. every load of the item is issued at once, the key side's first: the
+//      window keys and queries in the operand layout of the bf16 matrix
+//      instruction (16 columns x 32 key elements per step), the wave's key
+//      tile (ring history, then window keys), the gate inputs, the window
+//      values of the wave's rows, then its checkpoint rows and stored deltas;
+//   2. each wave normalises the window columns (norms reduced over the lanes
+//      that share a column) and its key rows, and forms their dot products on
+//      MFMA 16x16x32 bf16: raw bf16 keys give exact products summed in fp32
+//      (fp32 activations enter as bf16 high parts plus remainders, three
+//      products per step); wave 0 writes the normalised window columns to
+//      LDS and the window keys to the raw ring, and forms the gates and
+//      their prefix sums (DPP scan);
+//   3. (barrier) the coupling and output coefficients, over all threads;
+//   4. (barrier) each wave: S0 [kh_w, qh_w] for its 16 rows on MFMA 4x4x1
+//      straight from the checkpoint registers; the stored deltas meet the
+//      coefficients, four lane groups over the history, summed by lane
+//      swaps; each lane group runs the T-step window recurrence for the 16
+//      rows and writes every fourth output and delta.
+// Workgroups are not persistent: several items per compute unit are in
+// different phases at once, so one item's load latency is covered by the
+// others' arithmetic.  The items of one qk head (its value heads and value
+// parts read the same keys and window columns) get workgroup numbers equal
+// modulo 8, which puts them on one die and its L2.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -43,21 +57,38 @@ namespace gdn {
 
 namespace {
 
-constexpr int kDcWaves = 8;
+constexpr int kDcWaves = 4;                        // waves per workgroup (one item)
 constexpr int kDcThreads = 64 * kDcWaves;
-constexpr int kDcRows = 128;          // value rows per workgroup (16 per wave)
-constexpr int kDcGroups = kDcThreads / kDcRows;   // thread groups over the history
-// LDS arrays indexed by value row are stored column by column, so that the
-// lanes of a wave (consecutive value rows) touch consecutive banks.  The
-// column stride of SP is padded by 16 floats: its writes put four columns of
-// 16 rows in one instruction, on disjoint banks.
-constexpr int kSPS = kDcRows + 16;
-constexpr int kTMax = 16;             // window tokens at most (max_spec_len <= 16)
-constexpr int kDPre = 16;             // stored deltas per thread loaded at the start
+constexpr int kRPI = 16 * kDcWaves;                // value rows per item (a tile of 16 per wave)
+constexpr int kTMax = 16;                          // window tokens at most
+constexpr int kDPre = 16;                          // stored deltas per lane held in registers
 constexpr float kLog2eDc = 1.4426950408889634f;
 
+// Compile-time layout of one instantiation: activation type, key width K,
+// window capacity TM (4, 8 or 16 tokens), ring capacity LM (64 or 128).
+template <class Act, int K_, int TM_, int LM_>
+struct DcCfg {
+    static constexpr int K = K_, TM = TM_, LM = LM_;
+    static constexpr int eb = Act::bytes;
+    static constexpr bool kF32 = eb == 4;
+    static constexpr int KS = K / 32;              // matrix steps over the key
+    static constexpr int NCT = (2 * TM + 15) / 16; // 16-column groups of window columns
+    static constexpr int RPL = LM / 64;            // gate records per lane
+    static constexpr int NTW = LM / 64;            // 16-record key tiles per wave
+    // registers: checkpoint tile, deltas, window values, window and key
+    // operands (fp32 activations carry a remainder part too)
+    static constexpr int kRegs = K / 4 + kDPre + TM + (kF32 ? 2 : 1) * 4 * KS * (NCT + NTW) + 36;
+    // waves per SIMD: 6 (six workgroups per compute unit, 80 registers) for
+    // bf16 windows of up to 4 tokens on 64-record rings up to K = 128: the
+    // checkpoint rows are loaded after the key operands are consumed, so the
+    // two never hold registers at once; else 4 where the estimate fits 128
+    // registers, else 2.  More items per compute unit cover more of each
+    // item's load latency.
+    static constexpr int kMinWaves = (!kF32 && TM == 4 && LM == 64 && K <= 128) ? 6 : (kRegs <= 128 ? 4 : 2);
+};
+
 struct DcParams {
-    int B, T, TP, H, HV, V, L, num_slots, write_ring, nvt;
+    int B, T, TP, PC, H, HV, V, L, num_slots, write_ring, nparts, nunits;
     float scale, softplus_threshold, eps;
     const void *q, *k, *v, *a, *b;
     const float *A_log, *dt_bias;
@@ -70,12 +101,23 @@ struct DcParams {
     float* rb;
     float* rd;
     void* o;
-    // LDS carve-up, in floats
-    int KX;            // row stride of the window columns
-    int PC;            // columns per record: TP window keys, then TP queries
-    int o_x, o_gam, o_bet, o_wg, o_p, o_sp, o_part;
+    // the workgroup's LDS, in floats: X [PC][KX] normalised window keys
+    // (columns 0..TP-1) and queries (TP..2TP-1); P [L][PC] dot products,
+    // then coefficients; gam [L], bet [L]; SP [kDcWaves][PC][16] each wave's
+    // S0 products
+    int KX, o_p, o_gam, o_bet, o_sp;
 };
 
+// Read-only, wave-uniform metadata through the constant address space.
+template <class T>
+__device__ __forceinline__ T ldu(const T* ptr, size_t i)
+{
+    typedef const __attribute__((address_space(4))) T* cptr;
+    return ((cptr)ptr)[i];
+}
+
+// x plus its value in the paired 16-lane row (lane l ^ 16) or 32-lane half
+// (lane l ^ 32): every lane of the pair receives the same bits.
 __device__ __forceinline__ float swap16_sum_dc(float x)
 {
     const unsigned u = __float_as_uint(x);
@@ -92,288 +134,423 @@ __device__ __forceinline__ float swap32_sum_dc(float x)
     return __uint_as_float(lo) + __uint_as_float(hi);
 }
 
-// Sum over the eight lanes l + 8 c (c = 0..7) of a wave, delivered to each.
-__device__ __forceinline__ float rows8_sum_dc(float x)
+// Sum over the four lanes l % 16 + 16 q (q = 0..3), delivered to each.
+__device__ __forceinline__ float quarters_sum_dc(float x)
 {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
     return swap32_sum_dc(swap16_sum_dc(x));
 }
 
-// Activation element i of a row as fp32 (exact widening).
-template <class Act>
-__device__ __forceinline__ float act_at(const void* base, size_t i)
+// Sum over the eight lanes l % 8 + 8 c (c = 0..7), delivered to each.
+__device__ __forceinline__ float rows8_sum_dc(float x)
 {
-    return Act::load(static_cast<const typename Act::storage*>(base) + i);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    return quarters_sum_dc(x);
+}
+
+// DPP move of x; lanes without a source receive 0.
+template <int CTRL, int RM>
+__device__ __forceinline__ float dpp0_dc(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, RM, 0xF, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_scan_dc(float x)
+{
+    x += dpp0_dc<0x111, 0xF>(x);   // row_shr:1
+    x += dpp0_dc<0x112, 0xF>(x);   // row_shr:2
+    x += dpp0_dc<0x114, 0xF>(x);   // row_shr:4
+    x += dpp0_dc<0x118, 0xF>(x);   // row_shr:8
+    x += dpp0_dc<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp0_dc<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Eight consecutive activations of a key or query row: their raw bits (one
+// 16-byte load for bf16, two for fp32), loaded unconditionally (callers pass
+// a valid row for dead lanes and drop the values later): a load under a
+// branch, or arithmetic on the value right after it, makes the compiler wait
+// for it, and with it for every load issued before.
+template <class Act>
+struct RawChunk {
+    uint4 w[Act::bytes == 2 ? 1 : 2];
+};
+
+template <class Act>
+__device__ __forceinline__ RawChunk<Act> load_raw(const typename Act::storage* row, int e0)
+{
+    RawChunk<Act> c;
+    c.w[0] = *reinterpret_cast<const uint4*>(row + e0);
+    if constexpr (Act::bytes == 4)
+        c.w[1] = *reinterpret_cast<const uint4*>(row + e0 + 4);
+    return c;
+}
+
+// The chunk as the operand of a bf16 matrix step: the raw bits themselves
+// (bf16), or the bf16 rounding hi and the bf16 rounding of the remainder lo
+// (fp32).  ss gains the values' sum of squares.  Dead lanes carry the values
+// of a valid row; their products and norms are never stored.
+template <class Act>
+struct KeyChunk {
+    bf16x8 hi, lo;
+};
+
+template <class Act>
+__device__ __forceinline__ KeyChunk<Act> to_operand(const RawChunk<Act>& r, float& ss)
+{
+    KeyChunk<Act> c;
+    if constexpr (Act::bytes == 2) {
+        const uint4 w = r.w[0];
+        c.hi = __builtin_bit_cast(bf16x8, w);
+        c.lo = c.hi;
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 x = __builtin_bit_cast(bf16x2, u[e]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+        }
+    } else {
+        const uint4 w0 = r.w[0], w1 = r.w[1];
+        const float x[8] = {__uint_as_float(w0.x), __uint_as_float(w0.y), __uint_as_float(w0.z), __uint_as_float(w0.w),
+                            __uint_as_float(w1.x), __uint_as_float(w1.y), __uint_as_float(w1.z), __uint_as_float(w1.w)};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+            l[e] = pack_bf16x2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
+            ss = __builtin_fmaf(x[2 * e], x[2 * e], ss);
+            ss = __builtin_fmaf(x[2 * e + 1], x[2 * e + 1], ss);
+        }
+        c.hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+        c.lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
+    }
+    return c;
+}
+
+// The chunk's eight values as fp32 (exact for bf16; hi + lo for fp32).
+template <class Act>
+__device__ __forceinline__ void chunk_values(const KeyChunk<Act>& c, float (&x)[8])
+{
+    const uint4 h = __builtin_bit_cast(uint4, c.hi);
+    const uint32_t u[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(u[e] << 16);
+        x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+    if constexpr (Act::bytes == 4) {
+        const uint4 w = __builtin_bit_cast(uint4, c.lo);
+        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] += __uint_as_float(v[e] << 16);
+            x[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <class Act>
+__device__ __forceinline__ f32x4 key_product(const KeyChunk<Act>& a, const KeyChunk<Act>& b, f32x4 acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    if constexpr (Act::bytes == 4) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// The chunk's raw bits to the ring (its bit-exact record).
+template <class Act>
+__device__ __forceinline__ void store_raw(typename Act::storage* dst, const RawChunk<Act>& c)
+{
+    *reinterpret_cast<uint4*>(dst) = c.w[0];
+    if constexpr (Act::bytes == 4)
+        *reinterpret_cast<uint4*>(dst + 4) = c.w[1];
+}
+
+// Checkpoint rows r0 .. r0 + 15 of one (slot, value head): load i of lane l
+// reads row 8 (i & 1) + l % 8, key columns 32 (i >> 1) + 4 (l / 8) .. +3, so
+// every load instruction covers whole 128-byte lines.
+template <int K>
+__device__ __forceinline__ void load_tile(const float* rows, int lane, f32x4 (&sraw)[K / 16])
+{
+    const char* base = reinterpret_cast<const char*>(rows);
+    const uint32_t off = static_cast<uint32_t>(((lane & 7) * K + 4 * (lane >> 3)) * 4);
+#pragma unroll
+    for (int i = 0; i < K / 16; ++i)
+        sraw[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(base + ((i & 1) * 8 * K + (i >> 1) * 32) * 4 + off));
+}
+
+// Stored deltas of lane (row l % 16, group l / 16): records grp + 4 m, m <
+// kDPre.  Every load is issued (records past the history read the last one,
+// or record 0, again; their values are never used): loads under a branch
+// would turn the array into one register vector copied by every branch.
+__device__ __forceinline__ void load_deltas(const float* slab, int V, int L, int base, int hist, int lane,
+                                            float (&d)[kDPre])
+{
+    const int grp = lane >> 4;
+    const uint32_t off = static_cast<uint32_t>((lane & 15) * 4);
+    const int hl = hist > 0 ? hist - 1 : 0;
+#pragma unroll
+    for (int m = 0; m < kDPre; ++m) {
+        const int j = grp + 4 * m;
+        const int jc = j < hl ? j : hl;
+        const char* row = reinterpret_cast<const char*>(slab + static_cast<size_t>((base + jc) & (L - 1)) * V);
+        d[m] = *reinterpret_cast<const float*>(row + off);
+    }
 }
 
 }  // namespace
 
-// TM: window tokens at most for this instantiation (4, 8 or 16): the per-row
-// register arrays are sized by it.  Two workgroups per compute unit (128
-// VGPRs) up to K = 128; K = 256 holds twice the checkpoint registers and runs
-// one.
-template <class Act, int K, int TM>
-__global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_kernel(const DcParams p)
+template <class Act, int K, int TM, int LM, int MINW>
+__global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const DcParams p)
 {
+    using Cfg = DcCfg<Act, K, TM, LM>;
+    using st = typename Act::storage;
+    constexpr int KS = Cfg::KS, NCT = Cfg::NCT, NTW = Cfg::NTW;
     extern __shared__ __align__(16) float sm[];
-    float* Xs = sm + p.o_x;        // [PC][KX] normalised window keys, then queries
-    // Element k of a window column sits at xs_col(k): each quarter of the key
-    // (K / 4 elements, the share of one lane of a dot-product quad) is
-    // followed by 4 unused floats, so the quad's reads fall on distinct banks
-    // while each lane still reads (and loads) a contiguous quarter.  A row is
-    // K + 16 floats.
-    constexpr int KQ = K / 4;
-    auto xs_col = [](int k) { return k + 4 * (k / KQ); };
-    float* gam = sm + p.o_gam;     // [n] log2(e) * prefix sums of g (raw g until the scan)
-    float* bet = sm + p.o_bet;     // [n] beta
-    float* wg = sm + p.o_wg;       // [2 kTMax] window g then beta (for the ring)
-    float* P = sm + p.o_p;         // [L][PC] dot products, then coefficients
-    float* SP = sm + p.o_sp;       // [PC][kSPS] S0 times the window columns (column c, value row r)
-    float* part = sm + p.o_part;   // [kDcGroups - 1][2 kTMax][kDcRows] history partial sums
+    float* X = sm;
+    float* P = sm + p.o_p;
+    float* gam = sm + p.o_gam;
+    float* bet = sm + p.o_bet;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int item = blockIdx.x;
-    const int vt = item % p.nvt;
-    const int hv = (item / p.nvt) % p.HV;
-    const int b = item / p.nvt / p.HV;
-    const int s = p.slot_idx[b];
-    if (!valid_slot(s, p.num_slots))
-        return;                                    // padding row: nothing read or written
-    const int T = p.T, TP = p.TP, PC = p.PC, L = p.L, HV = p.HV, H = p.H, V = p.V;
-    const int G = HV / H, h = hv / G;
-    const bool flagged = p.is_flush[s] != 0;
-    const int wpc = clamp_wp(p.write_pos[s], L, T);
-    const int base = p.cache_base[s];
+    // item of this workgroup: blocks of 8 qk-head units x their per items,
+    // one unit per die (workgroup number mod 8)
+    const int G = p.HV / p.H;
+    const int per = G * p.nparts;
+    const int gx = static_cast<int>(blockIdx.x) & 7, gq = static_cast<int>(blockIdx.x) >> 3;
+    const int u = (gq / per) * 8 + gx, r = gq % per;
+    if (u >= p.nunits)
+        return;
+    const int b = u / p.H, h = u % p.H;
+    const int hv = h * G + r / p.nparts, part = r % p.nparts;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int grp = lane >> 4, rl = lane & 15;
+    const int T = p.T, H = p.H;
+    const st* kin = static_cast<const st*>(p.k);
+    const st* qin = static_cast<const st*>(p.q);
+    // ---- 1. loads.  The window columns first: they depend on the row and
+    // qk head only, so they are in flight while the slot's cursors are read.
+    // Column c = 16 ct + l % 16 (keys 0..T-1, then queries), key elements
+    // 32 ks + 8 (l / 16) .. +7; dead columns read window key 0.
+    RawChunk<Act> bcol_raw[NCT][KS];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = 16 * ct + rl;
+        const bool live = c < 2 * T;
+        const bool isq = live && c >= T;
+        const int t = live ? (isq ? c - T : c) : 0;
+        const st* row = (isq ? qin : kin) + ((static_cast<size_t>(b) * T + t) * H + h) * K;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bcol_raw[ct][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
+    }
+    const int s = ldu(p.slot_idx, b);
+    if (!valid_slot(s, p.num_slots)) {
+        // padding row: nothing written (the window columns in flight count as used)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < (Cfg::eb == 2 ? 1 : 2); ++e)
+                    asm volatile("" ::"v"(bcol_raw[ct][ks].w[e].x), "v"(bcol_raw[ct][ks].w[e].y),
+                                 "v"(bcol_raw[ct][ks].w[e].z), "v"(bcol_raw[ct][ks].w[e].w));
+        return;
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int TP = p.TP, PC = p.PC, L = p.L, KX = p.KX, V = p.V, HV = p.HV;
+    const bool flagged = ldu(p.is_flush, s) != 0;
+    const int wpc = clamp_wp(ldu(p.write_pos, s), L, T);
+    const int base = ldu(p.cache_base, s);
     const int hist = flagged ? 0 : wpc;
     const int n = hist + T;
-    const int v0 = vt * kDcRows;
-    const int BV = (V - v0) < kDcRows ? (V - v0) : kDcRows;
+    const int wp0 = base + wpc;
+    const int v0 = part * kRPI;
+    const int rows = (V - v0) < kRPI ? (V - v0) : kRPI;
+    const bool has_tile = 16 * wave < rows;
+    const int r0 = v0 + (has_tile ? 16 * wave : 0);
+    const bool wr = p.write_ring != 0;
+    const size_t head = static_cast<size_t>(s) * HV + hv;
+    st* ringk = static_cast<st*>(p.rawk) + (static_cast<size_t>(s) * H + h) * L * K;
 
-    // ---- 1. Loads, small ones first: the waits for the gate inputs, window
-    // values and window columns then never wait on the checkpoint stream
-    // behind them (vector-memory waits count loads in issue order).
-    const int grp = tid / kDcRows, vr = tid % kDcRows;   // (wave-uniform grp)
-    // gate inputs of the combined sequence (record j = tid < n): history from
-    // the ring, window a and b
-    float gin_a = 0.0f, gin_b = 0.0f;
-    const size_t gbase = (static_cast<size_t>(s) * HV + hv) * L;
-    const bool gate_thread = tid < n;
-    if (gate_thread) {
-        if (tid < hist) {
-            const int ph = (base + tid) & (L - 1);
-            gin_a = p.rg[gbase + ph];
-            gin_b = p.rb[gbase + ph];
-        } else {
-            const size_t tok = static_cast<size_t>(b) * T + (tid - hist);
-            gin_a = act_at<Act>(p.a, tok * HV + hv);
-            gin_b = act_at<Act>(p.b, tok * HV + hv);
-        }
+    // then this wave's key tiles, gate inputs, window values and deltas
+    RawChunk<Act> arow_raw[NTW][KS];
+#pragma unroll
+    for (int tw = 0; tw < NTW; ++tw) {
+        const int j = 16 * (wave + kDcWaves * tw) + rl;
+        const bool live = j < n;
+        // dead lanes read window key 0 (valid memory; dropped below)
+        const st* row = (live && j < hist) ? ringk + static_cast<size_t>((base + j) & (L - 1)) * K
+                                           : kin + ((static_cast<size_t>(b) * T + (live ? j - hist : 0)) * H + h) * K;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            arow_raw[tw][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
     }
-    // the window values of this thread's value row (used in step 5 by group 0)
-    float vwin[TM];
+    // gate inputs of records RPL lane + q (wave 0): raw bits of the ring's g
+    // and beta, or of the window's a and b (widened in step 2)
+    constexpr int RPL = Cfg::RPL;
+    typedef typename std::conditional<Cfg::eb == 2, uint16_t, uint32_t>::type actraw;
+    uint32_t ga[RPL], gb[RPL];
+    const size_t gslab = head * L;
+    if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-        vwin[i] = 0.0f;
-    if (grp == 0 && vr < BV) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int ic = i < T ? i : T - 1;
-            const size_t tok = static_cast<size_t>(b) * T + ic;
-            vwin[i] = act_at<Act>(p.v, (tok * HV + hv) * V + v0 + vr);
-        }
-    }
-    // the first window column of this wave (window keys are columns 0..TP-1,
-    // queries TP..2TP-1; zero past T)
-    auto column_loads = [&](int c, float (&x)[K / 64]) {
-        const bool isq = c >= TP;
-        const int t = isq ? c - TP : c;
-#pragma unroll
-        for (int e = 0; e < K / 64; ++e) {
-            x[e] = 0.0f;
-            if (t < T) {
-                const size_t tok = static_cast<size_t>(b) * T + t;
-                x[e] = act_at<Act>(isq ? p.q : p.k, (tok * H + h) * K + 64 * e + lane);
+        for (int q = 0; q < RPL; ++q) {
+            const int j = RPL * lane + q;
+            const int jc = j < n ? j : 0;
+            if (jc < hist) {
+                const int ph = (base + jc) & (L - 1);
+                ga[q] = reinterpret_cast<const uint32_t*>(p.rg)[gslab + ph];
+                gb[q] = reinterpret_cast<const uint32_t*>(p.rb)[gslab + ph];
+            } else {
+                const size_t idx = (static_cast<size_t>(b) * T + (jc - hist)) * HV + hv;
+                ga[q] = reinterpret_cast<const actraw*>(p.a)[idx];
+                gb[q] = reinterpret_cast<const actraw*>(p.b)[idx];
             }
         }
-    };
-    float x0[K / 64];
-    column_loads(wave < PC ? wave : 0, x0);
-    // checkpoint rows of this wave (in flight while the rest stages)
-    const bool has_rows = wave * 16 < BV;
-    const int r0 = v0 + (has_rows ? wave * 16 : 0);
-    const float* Srow = p.S + ((static_cast<size_t>(s) * HV + hv) * V + r0 + (lane & 7)) * K + 4 * (lane >> 3);
-    f32x4 sraw[K / 16];
-#pragma unroll
-    for (int i = 0; i < K / 16; ++i)
-        sraw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Srow + (i & 1) * 8 * K + (i >> 1) * 32));
-    // the stored deltas this thread sums in step 4 (records grp + kDcGroups m,
-    // the first kDPre of them); indices past the history are clamped to a
-    // valid record and skipped in step 4
-    const float* dring = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v0 + vr;
-    float dpre[kDPre];
-#pragma unroll
-    for (int m = 0; m < kDPre; ++m)
-        dpre[m] = 0.0f;
-    if (hist > 0 && vr < BV) {
-#pragma unroll
-        for (int m = 0; m < kDPre; ++m) {
-            const int j = grp + kDcGroups * m;
-            const int jc = j < hist ? j : hist - 1;
-            dpre[m] = dring[static_cast<size_t>((base + jc) & (L - 1)) * V];
-        }
     }
-
-    // window columns normalised into LDS, one wave per column
-    for (int c = wave; c < PC; c += kDcWaves) {
-        const bool isq = c >= TP;
-        const int t = isq ? c - TP : c;
-        float x[K / 64];
-        if (c == wave) {
+    st vw[TM];
+    {
+        const st* vb = static_cast<const st*>(p.v) + (static_cast<size_t>(b) * T * HV + hv) * V + r0 + rl;
 #pragma unroll
-            for (int e = 0; e < K / 64; ++e)
-                x[e] = x0[e];
-        } else {
-            column_loads(c, x);
-        }
+        for (int i = 0; i < TM; ++i)
+            vw[i] = vb[static_cast<size_t>(i < T ? i : T - 1) * HV * V];
+    }
+    float dpre[kDPre];
+    load_deltas(p.rd + head * L * V + r0, V, L, base, hist, lane, dpre);
+
+    // ---- 2. norms and dot products; X, gates and prefix sums (wave 0)
+    KeyChunk<Act> bcol[NCT][KS];
+    float rnc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const bool live = 16 * ct + rl < 2 * T;
         float ss = 0.0f;
 #pragma unroll
-        for (int e = 0; e < K / 64; ++e)
-            ss = __builtin_fmaf(x[e], x[e], ss);
-        ss = group_sum<64>(ss);
-        const float rn = t < T ? 1.0f / sqrtf(ss + p.eps) : 0.0f;
-#pragma unroll
-        for (int e = 0; e < K / 64; ++e)
-            Xs[c * p.KX + xs_col(64 * e + lane)] = x[e] * rn;
+        for (int ks = 0; ks < KS; ++ks)
+            bcol[ct][ks] = to_operand<Act>(bcol_raw[ct][ks], ss);
+        ss = quarters_sum_dc(ss);
+        rnc[ct] = live ? __builtin_amdgcn_rsqf(ss + p.eps) : 0.0f;
     }
-    // gates of the combined sequence: history as recorded, window computed
-    if (gate_thread) {
-        const int j = tid;
-        float g = gin_a, be = gin_b;
-        if (j >= hist) {
-            gdn_gate(gin_a, gin_b, p.A_log[hv], p.dt_bias[hv], p.softplus_threshold, g, be);
-            wg[j - hist] = g;
-            wg[kTMax + j - hist] = be;
-        }
-        gam[j] = g;
-        bet[j] = be;
-    }
-    __syncthreads();
-
-    // ---- 2a. prefix sums of the gates (wave 0; two records per lane, n <= 128)
     if (wave == 0) {
-        const int j0 = 2 * lane;
-        const float g0 = j0 < n ? gam[j0] : 0.0f;
-        const float g1 = j0 + 1 < n ? gam[j0 + 1] : 0.0f;
-        const float pair = g0 + g1;
-        float incl = pair;
+        const bool k_writer = wr && (hv % G == 0) && part == 0;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(incl, d, 64);
-            incl += lane >= d ? y : 0.0f;
-        }
-        const float excl = incl - pair;
-        // (all lanes read before any writes: the shuffles above synchronise the wave)
-        if (j0 < n)
-            gam[j0] = (excl + g0) * kLog2eDc;
-        if (j0 + 1 < n)
-            gam[j0 + 1] = (excl + g0 + g1) * kLog2eDc;
-    }
-    // ---- 2b. dot products of every record's key with the window columns:
-    // P[j][c] = kh_j . Xs[c] (history keys normalised here, window keys are
-    // the normalised columns themselves).  Four lanes share a product, each
-    // over a quarter of the key with all its loads issued first, and meet by
-    // quad swaps.
-    for (int t4 = tid; t4 < n * PC * 4; t4 += kDcThreads) {
-        const int sub = t4 & 3, task = t4 >> 2;
-        const int j = task / PC, c = task % PC;
-        const float* xc = Xs + c * p.KX + xs_col(sub * KQ);
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (j < hist) {
-            const int ph = (base + j) & (L - 1);
-            const typename Act::storage* kr = static_cast<const typename Act::storage*>(p.rawk) +
-                                              ((static_cast<size_t>(s) * H + h) * L + ph) * K + sub * KQ;
-            f32x4 kv[KQ / 4];
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = 16 * ct + rl;
+            if (c < 2 * T) {
+                const bool isq = c >= T;
+                const int t = isq ? c - T : c;
+                float* xc = X + (isq ? TP + t : t) * KX;
+                const float rn = rnc[ct];
 #pragma unroll
-            for (int e = 0; e < KQ / 4; ++e)
-                kv[e] = load4<Act>(kr + 4 * e);
-#pragma unroll
-            for (int e = 0; e < KQ / 4; ++e) {
-                const f32x4 xv = *reinterpret_cast<const f32x4*>(xc + 4 * e);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    ss[u] = __builtin_fmaf(kv[e][u], kv[e][u], ss[u]);
-                    acc[u] = __builtin_fmaf(kv[e][u], xv[u], acc[u]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    float x[8];
+                    chunk_values<Act>(bcol[ct][ks], x);
+                    float* dst = xc + 32 * ks + 8 * grp;
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{x[0] * rn, x[1] * rn, x[2] * rn, x[3] * rn};
+                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{x[4] * rn, x[5] * rn, x[6] * rn, x[7] * rn};
+                    if (!isq && k_writer)
+                        store_raw<Act>(ringk + static_cast<size_t>((wp0 + t) & (L - 1)) * K + 32 * ks + 8 * grp,
+                                       bcol_raw[ct][ks]);
                 }
             }
-        } else {
-            const float* xr = Xs + (j - hist) * p.KX + xs_col(sub * KQ);
-#pragma unroll
-            for (int e = 0; e < KQ / 4; ++e) {
-                const f32x4 kv = *reinterpret_cast<const f32x4*>(xr + 4 * e);
-                const f32x4 xv = *reinterpret_cast<const f32x4*>(xc + 4 * e);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    acc[u] = __builtin_fmaf(kv[u], xv[u], acc[u]);
-            }
         }
-        float a4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        float s4 = (ss[0] + ss[1]) + (ss[2] + ss[3]);
-        a4 += dpp<0xB1>(a4);          // quad_perm [1,0,3,2]
-        a4 += dpp<0x4E>(a4);          // quad_perm [2,3,0,1]
-        s4 += dpp<0xB1>(s4);
-        s4 += dpp<0x4E>(s4);
-        if (sub == 0)
-            P[j * PC + c] = j < hist ? a4 * (1.0f / sqrtf(s4 + p.eps)) : a4;
-    }
-    // ---- 2c. S0 [kh_w, qh_w] for this wave's 16 rows, four columns per group
-    if (has_rows) {
-        for (int cg = 0; cg < PC / 4; ++cg) {
-            const float* xrow = Xs + (4 * cg + (lane & 3)) * p.KX;
-            f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, b0 = a0, b1 = a0;
+        // window columns T..TP-1 and TP+T..2TP-1 are zero (their products are never read)
+        for (int e = lane; e < 2 * (TP - T) * K; e += 64) {
+            const int zc = e / K, kk = e % K;
+            X[(zc < TP - T ? T + zc : TP + T + (zc - (TP - T))) * KX + kk] = 0.0f;
+        }
+        // gates of the combined sequence: history as recorded, window formed
+        // here (and recorded in the ring by part 0); prefix sums
+        float gl[RPL], bl[RPL];
+        float pair = 0.0f;
 #pragma unroll
-            for (int i = 0; i < K / 16; ++i) {
-                const f32x4 za = *reinterpret_cast<const f32x4*>(xrow + xs_col(4 * (lane >> 3) + 32 * (i >> 1)));
-                if (i & 1) {
-                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a1, 0, 0, 0);
-                    b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b1, 0, 0, 0);
-                    a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a1, 0, 0, 0);
-                    b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b1, 0, 0, 0);
-                } else {
-                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
-                    b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b0, 0, 0, 0);
-                    a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
-                    b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b0, 0, 0, 0);
+        for (int q = 0; q < RPL; ++q) {
+            const int j = RPL * lane + q;
+            gl[q] = 0.0f;
+            bl[q] = 0.0f;
+            if (j < hist) {
+                gl[q] = __uint_as_float(ga[q]);
+                bl[q] = __uint_as_float(gb[q]);
+            } else if (j < n) {
+                const float a_in = Cfg::eb == 2 ? __uint_as_float(ga[q] << 16) : __uint_as_float(ga[q]);
+                const float b_in = Cfg::eb == 2 ? __uint_as_float(gb[q] << 16) : __uint_as_float(gb[q]);
+                gdn_gate(a_in, b_in, ldu(p.A_log, hv), ldu(p.dt_bias, hv), p.softplus_threshold, gl[q], bl[q]);
+                if (wr && part == 0) {
+                    const int ph = (wp0 + j - hist) & (L - 1);
+                    p.rg[gslab + ph] = gl[q];
+                    p.rb[gslab + ph] = bl[q];
                 }
             }
-            // lane l, register r: column 4 cg + r of row 8 hh + l % 8 (hh = 0:
-            // a0 + b0, 1: a1 + b1), partial over key group l / 8
-            const f32x4 lo = a0 + b0, hi = a1 + b1;
-            const int c = lane >> 3;
-            float val = 0.0f;
+            pair += gl[q];
+        }
+        float run = wave_scan_dc(pair) - pair;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sl = rows8_sum_dc(lo[r]), sh = rows8_sum_dc(hi[r]);
-                val = c == r ? sl : (c == 4 + r ? sh : val);
+        for (int q = 0; q < RPL; ++q) {
+            const int j = RPL * lane + q;
+            run += gl[q];
+            if (j < n) {
+                gam[j] = run * kLog2eDc;
+                bet[j] = bl[q];
             }
-            const int row = wave * 16 + (lane & 7) + 8 * (c >> 2);
-            SP[(4 * cg + (c & 3)) * kSPS + row] = val;
         }
     }
+    // this wave's key tiles against the window columns; lane l, register q:
+    // record 16 (wave + 4 tw) + 4 (l / 16) + q, column 16 ct + l % 16
+#pragma unroll
+    for (int tw = 0; tw < NTW; ++tw) {
+        const int j0 = 16 * (wave + kDcWaves * tw);
+        const bool live = j0 + rl < n;
+        KeyChunk<Act> arow[KS];
+        float ss = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            arow[ks] = to_operand<Act>(arow_raw[tw][ks], ss);
+        const float rnj = live ? __builtin_amdgcn_rsqf(quarters_sum_dc(ss) + p.eps) : 0.0f;
+        float rnr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            rnr[q] = __shfl(rnj, 4 * grp + q, 64);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = key_product<Act>(arow[ks], bcol[ct][ks], acc);
+            const int c = 16 * ct + rl;
+            if (c < 2 * T) {
+                const int col = c < T ? c : TP + (c - T);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int jr = j0 + 4 * grp + q;
+                    if (jr < n)
+                        P[jr * PC + col] = acc[q] * rnr[q] * rnc[ct];
+                }
+            }
+        }
+    }
+    // the checkpoint rows, issued once the key operands' registers are free:
+    // their latency overlaps the coefficient phase, and the lower register
+    // peak lets more workgroups share a compute unit
+    f32x4 sraw[K / 16];
+    load_tile<K>(p.S + (head * V + r0) * K, lane, sraw);
     __syncthreads();
 
     // ---- 3. coefficients: column i < T of record j couples window token i to
     // j (j < hist + i): beta e^{Gam_{h+i} - Gam_j} kh_i . kh_j; query column t
     // weighs d_j in output t (j <= hist + t): e^{Gam_{h+t} - Gam_j} kh_j . qh_t
     for (int task = tid; task < n * PC; task += kDcThreads) {
-        const int j = task / PC, c = task % PC;
-        const bool isq = c >= TP;
-        const int t = isq ? c - TP : c;
+        const int j = task / PC, col = task - j * PC;
+        const bool isq = col >= TP;
+        const int t = isq ? col - TP : col;
         float coef = 0.0f;
         if (t < T) {
             const int i = hist + t;
-            const bool live = isq ? j <= i : j < i;
-            if (live) {
-                const float w = exp2f(gam[i] - gam[j]);
+            if (isq ? j <= i : j < i) {
+                const float w = __builtin_amdgcn_exp2f(gam[i] - gam[j]);
                 coef = (isq ? w : bet[i] * w) * P[task];
             }
         }
@@ -381,163 +558,173 @@ __global__ __launch_bounds__(kDcThreads, K >= 256 ? 2 : 4) void dcache_verify_ke
     }
     __syncthreads();
 
-    // ---- 4. history through the stored deltas: each thread group takes
-    // every kDcGroups-th record for its value row (the first kDPre from the
-    // registers loaded at the start)
+    // ---- 4. this wave's tile
+    if (!has_tile) {
+#pragma unroll
+        for (int i = 0; i < K / 16; ++i)
+            asm volatile("" ::"v"(sraw[i][0]), "v"(sraw[i][1]), "v"(sraw[i][2]), "v"(sraw[i][3]));
+#pragma unroll
+        for (int m = 0; m < kDPre; ++m)
+            asm volatile("" ::"v"(dpre[m]));
+        return;
+    }
+    float* SPl = sm + p.o_sp + wave * PC * 16;
+    // S0 [kh_w, qh_w] for the tile's rows, four columns per group; lane l,
+    // register q of the sums: column 4 cg + q of row 8 hh + l % 8 (hh = 0:
+    // even loads, 1: odd), partial over key group l / 8
+    for (int cg = 0; cg < PC / 4; ++cg) {
+        const float* xrow = X + (4 * cg + (lane & 3)) * KX + 4 * (lane >> 3);
+        f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, b0 = a0, b1 = a0;
+#pragma unroll
+        for (int i = 0; i < K / 16; ++i) {
+            const f32x4 za = *reinterpret_cast<const f32x4*>(xrow + 32 * (i >> 1));
+            if (i & 1) {
+                a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a1, 0, 0, 0);
+                b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b1, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a1, 0, 0, 0);
+                b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b1, 0, 0, 0);
+            } else {
+                a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
+                b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b0, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
+                b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b0, 0, 0, 0);
+            }
+        }
+        const f32x4 lo = a0 + b0, hi = a1 + b1;
+        const int c = lane >> 3;
+        float val = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float sl = rows8_sum_dc(lo[q]), sh = rows8_sum_dc(hi[q]);
+            val = c == q ? sl : (c == 4 + q ? sh : val);
+        }
+        SPl[(4 * cg + (c & 3)) * 16 + (lane & 7) + 8 * (c >> 2)] = val;
+    }
+    // stored deltas against the coefficients: lane group grp takes records
+    // grp + 4 m of row rl; the four groups meet by lane swaps
     float hA[TM], hF[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
         hA[t] = 0.0f;
         hF[t] = 0.0f;
     }
-    if (vr < BV) {
 #pragma unroll
-        for (int m = 0; m < kDPre; ++m) {
-            const int j = grp + kDcGroups * m;
-            if (j < hist) {                      // wave-uniform
-                const float dj = dpre[m];
-                const float* cj = P + j * PC;
-#pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    if (t < T) {
-                        hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
-                        hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
-                    }
-                }
-            }
-        }
-        for (int j = grp + kDcGroups * kDPre; j < hist; j += kDcGroups) {
-            const float dj = dring[static_cast<size_t>((base + j) & (L - 1)) * V];
-            const float* cj = P + j * PC;
+    for (int m = 0; m < kDPre; ++m) {
+        const int j = grp + 4 * m;
+        if (4 * m < hist) {                      // uniform; records past hist weigh nothing
+            const float dj = j < hist ? dpre[m] : 0.0f;
+            const float* cj = P + (j < hist ? j : 0) * PC;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                if (t < T) {
-                    hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
-                    hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
-                }
-            }
-        }
-        if (grp > 0) {
-            float* pr = part + (grp - 1) * 2 * kTMax * kDcRows + vr;
-#pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                if (t < T) {
-                    pr[t * kDcRows] = hA[t];
-                    pr[(kTMax + t) * kDcRows] = hF[t];
-                }
+                hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
+                hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
             }
         }
     }
-    __syncthreads();
-
-    // ---- 5. window deltas and outputs (group 0, one thread per value row);
-    // raw records to the ring (other groups)
-    const int wp_phys0 = base + wpc;
-    if (grp == 0) {
-        if (vr < BV) {
-#pragma unroll
-            for (int gq = 1; gq < kDcGroups; ++gq) {
-                const float* pr = part + (gq - 1) * 2 * kTMax * kDcRows + vr;
-#pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    if (t < T) {
-                        hA[t] += pr[t * kDcRows];
-                        hF[t] += pr[(kTMax + t) * kDcRows];
-                    }
-                }
-            }
-            const int v = v0 + vr;
-            float dw[TM];
-            const float* spr = SP + vr;
-            using st = typename Act::storage;
-            st* out = static_cast<st*>(p.o);
-            float* dout = p.rd + (static_cast<size_t>(s) * HV + hv) * L * V + v;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                dw[i] = 0.0f;
-                if (i < T) {
-                    const int ii = hist + i;
-                    float d = bet[ii] * (vwin[i] - exp2f(gam[ii]) * spr[i * kSPS]) - hA[i];
-#pragma unroll
-                    for (int i2 = 0; i2 < TM; ++i2)
-                        if (i2 < i)
-                            d = __builtin_fmaf(-P[(hist + i2) * PC + i], dw[i2], d);
-                    dw[i] = d;
-                    if (p.write_ring)
-                        dout[static_cast<size_t>((wp_phys0 + i) & (L - 1)) * V] = d;
-                }
-            }
+    if constexpr (LM - 1 > 4 * kDPre) {
+        // records past the registers (rings longer than 64 records)
+        const float* dslab = p.rd + head * L * V + r0 + rl;
+        for (int m = kDPre; 4 * m < hist; ++m) {
+            const int j = grp + 4 * m;
+            const int jc = j < hist ? j : hist - 1;
+            const float dv = dslab[static_cast<size_t>((base + jc) & (L - 1)) * V];
+            const float dj = j < hist ? dv : 0.0f;
+            const float* cj = P + jc * PC;
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                if (t < T) {
-                    const int it = hist + t;
-                    float acc = exp2f(gam[it]) * spr[(TP + t) * kSPS] + hF[t];
+                hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
+                hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
+            }
+        }
+    }
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        if (i <= t)
-                            acc = __builtin_fmaf(P[(hist + i) * PC + TP + t], dw[i], acc);
-                    const size_t tok = static_cast<size_t>(b) * T + t;
-                    out[(tok * HV + hv) * V + v] = Act::from_f32(p.scale * acc);
-                }
-            }
+    for (int t = 0; t < TM; ++t) {
+        hA[t] = quarters_sum_dc(hA[t]);
+        hF[t] = quarters_sum_dc(hF[t]);
+    }
+    // window deltas of row r0 + rl (every group forms all T of them) and the
+    // outputs; lane group grp writes window positions and outputs grp + 4 m
+    st* out = static_cast<st*>(p.o);
+    const int v = r0 + rl;
+    float dw[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        dw[i] = 0.0f;
+        if (i < T) {
+            const int ii = hist + i;
+            float vi;
+            if constexpr (Act::bytes == 2)
+                vi = bf16_to_f32(vw[i]);
+            else
+                vi = vw[i];
+            float d = bet[ii] * (vi - __builtin_amdgcn_exp2f(gam[ii]) * SPl[i * 16 + rl]) - hA[i];
+#pragma unroll
+            for (int i2 = 0; i2 < TM; ++i2)
+                if (i2 < i)
+                    d = __builtin_fmaf(-P[(hist + i2) * PC + i], dw[i2], d);
+            dw[i] = d;
+            if (wr && (i & 3) == grp)
+                p.rd[(gslab + ((wp0 + i) & (L - 1))) * V + v] = d;
         }
-    } else if (p.write_ring) {
-        // pre-mutation raw bits of the window: keys once per qk head (value
-        // head hv % G == 0, value tile 0), this tile's values, gates (tile 0)
-        using st = typename Act::storage;
-        const int rt = tid - kDcRows;                 // 0 .. 3 kDcRows - 1
-        const int nrt = kDcThreads - kDcRows;
-        const st* kwin = static_cast<const st*>(p.k);
-        const st* vwin = static_cast<const st*>(p.v);
-        st* rk = static_cast<st*>(p.rawk) + (static_cast<size_t>(s) * H + h) * L * K;
-        st* rv = static_cast<st*>(p.rawv) + (static_cast<size_t>(s) * HV + hv) * L * V + v0;
-        if (hv % G == 0 && vt == 0) {
-            for (int e = rt; e < T * K; e += nrt) {
-                const int t = e / K, c = e % K;
-                const size_t tok = static_cast<size_t>(b) * T + t;
-                rk[static_cast<size_t>((wp_phys0 + t) & (L - 1)) * K + c] = kwin[(tok * H + h) * K + c];
-            }
-        }
-        for (int e = rt; e < T * BV; e += nrt) {
-            const int t = e / BV, c = e % BV;
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        if (t < T && (t & 3) == grp) {
+            const int i = hist + t;
+            float acc = __builtin_amdgcn_exp2f(gam[i]) * SPl[(TP + t) * 16 + rl] + hF[t];
+#pragma unroll
+            for (int i2 = 0; i2 < TM; ++i2)
+                if (i2 <= t)
+                    acc = __builtin_fmaf(P[(hist + i2) * PC + TP + t], dw[i2], acc);
             const size_t tok = static_cast<size_t>(b) * T + t;
-            rv[static_cast<size_t>((wp_phys0 + t) & (L - 1)) * V + c] = vwin[(tok * HV + hv) * V + v0 + c];
-        }
-        if (vt == 0 && rt < T) {
-            const int ph = (wp_phys0 + rt) & (L - 1);
-            p.rg[gbase + ph] = wg[rt];
-            p.rb[gbase + ph] = wg[kTMax + rt];
+            out[(tok * HV + hv) * V + v] = Act::from_f32(p.scale * acc);
         }
     }
-    // the checkpoint registers of waves without rows count as consumed
-    if (!has_rows) {
+    // the window values of the tile's rows to the raw ring (lane group grp
+    // takes window positions grp + 4 m)
+    if (wr) {
+        st* rv = static_cast<st*>(p.rawv);
 #pragma unroll
-        for (int i = 0; i < K / 16; ++i)
-            asm volatile("" ::"v"(sraw[i][0]), "v"(sraw[i][1]), "v"(sraw[i][2]), "v"(sraw[i][3]));
+        for (int i = 0; i < TM; ++i)
+            if (i < T && (i & 3) == grp)
+                rv[(gslab + ((wp0 + i) & (L - 1))) * V + v] = vw[i];
     }
 }
 
 // ------------------------------------------------------------------- host
 
-size_t dcache_lds_bytes(const gdn_shape& sh)
+namespace {
+
+struct DcLayout {
+    int TP, PC, KX, o_p, o_gam, o_bet, o_sp, total;   // floats
+};
+
+DcLayout dc_layout(const gdn_shape& sh)
 {
-    const int TP = (sh.T + 3) & ~3;
-    const int PC = 2 * TP;
-    const int KX = sh.K + 16;
-    size_t f = 0;
-    f += static_cast<size_t>(PC) * KX;               // Xs
-    f += 2 * static_cast<size_t>(sh.L);              // gam, bet
-    f += 2 * kTMax;                                  // wg
-    f += static_cast<size_t>(sh.L) * PC;             // P
-    f += static_cast<size_t>(PC) * kSPS;             // SP
-    f += static_cast<size_t>(kDcGroups - 1) * kDcRows * 2 * kTMax;   // part
-    return f * 4;
+    DcLayout d;
+    d.TP = (sh.T + 3) & ~3;
+    d.PC = 2 * d.TP;
+    d.KX = sh.K + 16;   // rows read four at a time as 16-byte groups: a 64-byte pad keeps them off each other's banks
+    d.o_p = d.PC * d.KX;
+    d.o_gam = d.o_p + sh.L * d.PC;
+    d.o_bet = d.o_gam + sh.L;
+    d.o_sp = (d.o_bet + sh.L + 3) & ~3;
+    d.total = d.o_sp + kDcWaves * d.PC * 16;
+    return d;
 }
 
-template <class Act, int K, int TM>
+}  // namespace
+
+size_t dcache_lds_bytes(const gdn_shape& sh)
+{
+    return static_cast<size_t>(dc_layout(sh).total) * 4;
+}
+
+template <class Act, int K, int TM, int LM>
 static hipError_t launch_dc_k(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
 {
-    auto kern = dcache_verify_kernel<Act, K, TM>;
+    using Cfg = DcCfg<Act, K, TM, LM>;
+    auto kern = dcache_verify_kernel<Act, K, TM, LM, Cfg::kMinWaves>;
     const size_t lds = dcache_lds_bytes(sh);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -546,28 +733,35 @@ static hipError_t launch_dc_k(const gdn_shape& sh, const DcParams& p, hipStream_
         if (e != hipSuccess)
             return e;
     }
-    const unsigned grid = static_cast<unsigned>(sh.B) * sh.HV * p.nvt;
+    // blocks of 8 qk-head units, each unit's items one per row of 8
+    const long long per = static_cast<long long>(sh.HV / sh.H) * p.nparts;
+    const long long blocks = (static_cast<long long>(p.nunits) + 7) / 8;
+    const unsigned grid = static_cast<unsigned>(blocks * 8 * per);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kDcThreads), lds, stream, p);
     return hipGetLastError();
 }
 
-template <class Act, int K>
+template <class Act, int K, int LM>
 static hipError_t launch_dc_t(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
 {
     if (sh.T <= 4)
-        return launch_dc_k<Act, K, 4>(sh, p, stream);
+        return launch_dc_k<Act, K, 4, LM>(sh, p, stream);
     if (sh.T <= 8)
-        return launch_dc_k<Act, K, 8>(sh, p, stream);
-    return launch_dc_k<Act, K, kTMax>(sh, p, stream);
+        return launch_dc_k<Act, K, 8, LM>(sh, p, stream);
+    return launch_dc_k<Act, K, kTMax, LM>(sh, p, stream);
 }
 
 template <class Act>
 static hipError_t launch_dc_act(const gdn_shape& sh, const DcParams& p, hipStream_t stream)
 {
+    const bool big = sh.L > 64;
     switch (sh.K) {
-    case 64: return launch_dc_t<Act, 64>(sh, p, stream);
-    case 128: return launch_dc_t<Act, 128>(sh, p, stream);
-    case 256: return launch_dc_t<Act, 256>(sh, p, stream);
+    case 64: return big ? launch_dc_t<Act, 64, 128>(sh, p, stream) : launch_dc_t<Act, 64, 64>(sh, p, stream);
+    case 128: return big ? launch_dc_t<Act, 128, 128>(sh, p, stream) : launch_dc_t<Act, 128, 64>(sh, p, stream);
+    case 256:
+        if (big)
+            return hipErrorInvalidValue;
+        return launch_dc_t<Act, 256, 64>(sh, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -578,17 +772,20 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
 {
     if (sh.B == 0)
         return hipSuccess;
+    const DcLayout lay = dc_layout(sh);
     DcParams p = {};
     p.B = sh.B;
     p.T = sh.T;
-    p.TP = (sh.T + 3) & ~3;
+    p.TP = lay.TP;
+    p.PC = lay.PC;
     p.H = sh.H;
     p.HV = sh.HV;
     p.V = sh.V;
     p.L = sh.L;
     p.num_slots = sh.num_slots;
     p.write_ring = write_ring;
-    p.nvt = (sh.V + kDcRows - 1) / kDcRows;
+    p.nparts = (sh.V + kRPI - 1) / kRPI;
+    p.nunits = sh.B * sh.H;
     p.scale = sh.scale;
     p.softplus_threshold = sh.softplus_threshold;
     p.eps = sh.l2norm_eps;
@@ -610,15 +807,11 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
     p.rb = r.beta;
     p.rd = ring_d;
     p.o = o;
-    p.PC = 2 * p.TP;
-    p.KX = sh.K + 16;   // rows read four at a time as 16-byte groups: a 64-byte pad keeps them off each other's banks
-    p.o_x = 0;
-    p.o_gam = p.o_x + p.PC * p.KX;
-    p.o_bet = p.o_gam + sh.L;
-    p.o_wg = p.o_bet + sh.L;
-    p.o_p = p.o_wg + 2 * kTMax;
-    p.o_sp = p.o_p + sh.L * p.PC;
-    p.o_part = p.o_sp + p.PC * kSPS;
+    p.KX = lay.KX;
+    p.o_p = lay.o_p;
+    p.o_gam = lay.o_gam;
+    p.o_bet = lay.o_bet;
+    p.o_sp = lay.o_sp;
     return sh.act == GDN_BF16 ? launch_dc_act<ActBF16>(sh, p, stream)
                               : launch_dc_act<ActF32>(sh, p, stream);
 }
