@@ -35,8 +35,8 @@
 //      MFMA 16x16x32 bf16: raw bf16 keys give exact products summed in fp32
 //      (fp32 activations enter as bf16 high parts plus remainders, three
 //      products per step); wave 0 writes the normalised window columns to
-//      LDS and the window keys to the raw ring, and forms the gates and
-//      their prefix sums (DPP scan);
+//      LDS and the window keys to the raw ring, the last wave forms the gates
+//      and their prefix sums (DPP scan);
 //   3. (barrier) the coupling and output coefficients, over all threads;
 //   4. (barrier) each wave: S0 [kh_w, qh_w] for its 16 rows on MFMA 4x4x1
 //      straight from the checkpoint registers; the stored deltas meet the
@@ -390,13 +390,13 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
         for (int ks = 0; ks < KS; ++ks)
             arow_raw[tw][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
     }
-    // gate inputs of records RPL lane + q (wave 0): raw bits of the ring's g
-    // and beta, or of the window's a and b (widened in step 2)
+    // gate inputs of records RPL lane + q (last wave): raw bits of the ring's
+    // g and beta, or of the window's a and b (widened in step 2)
     constexpr int RPL = Cfg::RPL;
     typedef typename std::conditional<Cfg::eb == 2, uint16_t, uint32_t>::type actraw;
     uint32_t ga[RPL], gb[RPL];
     const size_t gslab = head * L;
-    if (wave == 0) {
+    if (wave == kDcWaves - 1) {
 #pragma unroll
         for (int q = 0; q < RPL; ++q) {
             const int j = RPL * lane + q;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
     float dpre[kDPre];
     load_deltas(p.rd + head * L * V + r0, V, L, base, hist, lane, dpre);
 
-    // ---- 2. norms and dot products; X, gates and prefix sums (wave 0)
+    // ---- 2. norms and dot products; X (wave 0); gates and prefix sums (last wave)
     KeyChunk<Act> bcol[NCT][KS];
     float rnc[NCT];
 #pragma unroll
@@ -463,6 +463,8 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             const int zc = e / K, kk = e % K;
             X[(zc < TP - T ? T + zc : TP + T + (zc - (TP - T))) * KX + kk] = 0.0f;
         }
+    }
+    if (wave == kDcWaves - 1) {
         // gates of the combined sequence: history as recorded, window formed
         // here (and recorded in the ring by part 0); prefix sums
         float gl[RPL], bl[RPL];
