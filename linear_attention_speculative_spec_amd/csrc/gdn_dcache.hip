@@ -644,8 +644,11 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
         hA[t] = quarters_sum_dc(hA[t]);
         hF[t] = quarters_sum_dc(hF[t]);
     }
-    // window deltas of row r0 + rl (every group forms all T of them) and the
-    // outputs; lane group grp writes window positions and outputs grp + 4 m
+    // window deltas of row r0 + rl: every lane forms all T of them (the
+    // recurrence); lane group grp then takes window positions and tokens
+    // t = grp + 4 m with uniform code (per-lane LDS indices and selects over
+    // the registers: one branch per token would be issued by every lane
+    // group), writing the output, the delta and the raw value
     st* out = static_cast<st*>(p.o);
     const int v = r0 + rl;
     float dw[TM];
@@ -665,31 +668,37 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
                 if (i2 < i)
                     d = __builtin_fmaf(-P[(hist + i2) * PC + i], dw[i2], d);
             dw[i] = d;
-            if (wr && (i & 3) == grp)
-                p.rd[(gslab + ((wp0 + i) & (L - 1))) * V + v] = d;
         }
     }
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        if (t < T && (t & 3) == grp) {
-            const int i = hist + t;
-            float acc = __builtin_amdgcn_exp2f(gam[i]) * SPl[(TP + t) * 16 + rl] + hF[t];
+    for (int m = 0; m < (TM + 3) / 4; ++m) {
+        const int t = grp + 4 * m;
+        const int tc = t < T ? t : T - 1;          // dead lanes read a valid token
+        const int i = hist + tc;
+        float hsel = 0.0f, dsel = 0.0f;
+        st vsel = vw[0];
 #pragma unroll
-            for (int i2 = 0; i2 < TM; ++i2)
-                if (i2 <= t)
-                    acc = __builtin_fmaf(P[(hist + i2) * PC + TP + t], dw[i2], acc);
+        for (int u = 0; u < TM; ++u) {
+            hsel = tc == u ? hF[u] : hsel;
+            dsel = tc == u ? dw[u] : dsel;
+            vsel = tc == u ? vw[u] : vsel;
+        }
+        float acc = __builtin_amdgcn_exp2f(gam[i]) * SPl[(TP + tc) * 16 + rl] + hsel;
+#pragma unroll
+        for (int u = 0; u < TM; ++u) {
+            const int ju = hist + u < n ? hist + u : n - 1;
+            const float f = __builtin_fmaf(P[ju * PC + TP + tc], dw[u], acc);
+            acc = u <= tc ? f : acc;
+        }
+        if (t < T) {
             const size_t tok = static_cast<size_t>(b) * T + t;
             out[(tok * HV + hv) * V + v] = Act::from_f32(p.scale * acc);
+            if (wr) {
+                const size_t ri = (gslab + ((wp0 + t) & (L - 1))) * V + v;
+                p.rd[ri] = dsel;
+                static_cast<st*>(p.rawv)[ri] = vsel;
+            }
         }
-    }
-    // the window values of the tile's rows to the raw ring (lane group grp
-    // takes window positions grp + 4 m)
-    if (wr) {
-        st* rv = static_cast<st*>(p.rawv);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            if (i < T && (i & 3) == grp)
-                rv[(gslab + ((wp0 + i) & (L - 1))) * V + v] = vw[i];
     }
 }
 
