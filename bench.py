@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--summarize-kda-profile", metavar="DIR",
                     help="no GPU work: write the KDA kernel's profile summary from the rocprofv3 "
                          "CSVs under DIR/kt and DIR/alu")
+    ap.add_argument("--summarize-dcache-profile", metavar="DIR",
+                    help="no GPU work: write the d-cache verify's profile summary from the rocprofv3 "
+                         "CSVs under DIR/kt, DIR/fetch, DIR/write and DIR/alu")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="no GPU work: write the profile summary from the rocprofv3 CSVs "
                          "under DIR/kt, DIR/fetch and DIR/write")
@@ -182,6 +185,9 @@ def main():
         return
     if args.summarize_kda_profile:
         summarize_kda_profile(args.summarize_kda_profile)
+        return
+    if args.summarize_dcache_profile:
+        summarize_dcache_profile(args.summarize_dcache_profile)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -887,6 +893,131 @@ def summarize_kda_profile(d):
                    f"{flops / valu:.1f} flops per wave-level VALU instruction (at most 128).")
     os.makedirs(os.path.dirname(KDA_PROFILE_SUMMARY), exist_ok=True)
     with open(KDA_PROFILE_SUMMARY, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+DCACHE_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "dcache_verify_kernel_qwen3next_b256.md")
+DCACHE_SRC = os.path.join(ROOT, "linear_attention_speculative_spec_amd", "csrc", "gdn_dcache.hip")
+_DC_LEG = "--no-cpu-baseline --no-snapshot --no-fold-every-commit --no-kda --no-chain --copy-calibration"
+DCACHE_PROFILE_CMDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/dcprof/kt -o run --output-format csv -- "
+    f"python3 $R/bench.py --steps 50 --warmup 20 {_DC_LEG} > $R/gpurun_out/dcprof/kt.log 2>&1",
+    "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/dcprof/fetch -o run --output-format csv -- "
+    f"python3 $R/bench.py --steps 5 --warmup 2 {_DC_LEG}",
+    "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/dcprof/write -o run --output-format csv -- "
+    f"python3 $R/bench.py --steps 5 --warmup 2 {_DC_LEG}",
+    "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY "
+    "SQ_WAIT_ANY GRBM_GUI_ACTIVE -d $R/gpurun_out/dcprof/alu -o run --output-format csv -- "
+    f"python3 $R/bench.py --steps 5 --warmup 2 {_DC_LEG}",
+    "cd $R && python3 bench.py --summarize-dcache-profile gpurun_out/dcprof",
+]
+
+
+def summarize_dcache_profile(d):
+    """Profile summary (markdown) of the d-cache verify kernel: its average
+    duration over the timed steps of the d-cache leg, its HBM bytes from the
+    byte counters (scaled by a plain copy's), and its instruction counters
+    against the vector issue rate."""
+    steps_kt, steps_pmc = 50, 5
+
+    def is_dc(r):
+        return "dcache_verify_kernel" in r["Kernel_Name"]
+
+    trace = [r for r in _csv(os.path.join(d, "kt", "run_kernel_trace.csv")) if is_dc(r)]
+    stats = _csv(os.path.join(d, "kt", "run_kernel_stats.csv"))
+    big = max(int(r["Grid_Size_X"]) for r in trace)          # the B=256 windows (the pre-fill runs T=1)
+    timed = [r for r in trace if int(r["Grid_Size_X"]) == big][-steps_kt:]
+    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed]) * 1e-3
+    kname = timed[-1]["Kernel_Name"]
+
+    def counter(sub, name, copy=True):
+        rows = [r for r in _csv(os.path.join(d, sub, "run_counter_collection.csv")) if r["Counter_Name"] == name]
+        g = max(int(r["Grid_Size"]) for r in rows if is_dc(r))
+        v = [float(r["Counter_Value"]) for r in rows if is_dc(r) and int(r["Grid_Size"]) == g][-steps_pmc:]
+        # the calibration copies: the first three copy dispatches after the
+        # headline leg's last verify (the d-cache leg that follows restores its
+        # state with copies of its own)
+        last_v = max(int(r["Dispatch_Id"]) for r in rows
+                     if "verify_kernel" in r["Kernel_Name"] and not is_dc(r))
+        cr = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                    if "copy" in r["Kernel_Name"].lower() and int(r["Dispatch_Id"]) > last_v)[:3]
+        c = [x for _, x in cr]
+        return float(np.mean(v)), float(np.mean(c if copy else [1.0]))
+
+    fv, fc = counter("fetch", "FETCH_SIZE")
+    wv, wc = counter("write", "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    f_fetch, f_write = kib / fc, kib / wc
+    hbm = (fv * f_fetch + wv * f_write) * 1024.0
+    alg = None
+    try:
+        for line in open(os.path.join(d, "kt.log")):
+            if line.startswith("{"):
+                alg = json.loads(line)["dcache"]["alg_bytes_per_launch"]
+    except (OSError, KeyError):
+        pass
+    src_hash = hashlib.sha256(open(DCACHE_SRC, "rb").read()).hexdigest()[:16]
+    t = dur.mean() * 1e-6
+    out = ["# dcache_verify_kernel, GDN layer B=256 (qwen3next_b256 workload)\n",
+           "The d-cache verify (`gdn_spec_verify_dcache`): history read through stored corrected deltas. "
+           "It is timed in `bench.py`'s `dcache` leg on the same checkpoint, cursors, windows and accept "
+           "counts as the headline.\n",
+           "Commands (from the repository root on the GPU host, `R=$PWD`; each profiler run under "
+           "its own `timeout`):\n",
+           "```\n" + "\n".join(DCACHE_PROFILE_CMDS) + "\n```\n",
+           f"- kernel source: `linear_attention_speculative_spec_amd/csrc/gdn_dcache.hip`, "
+           f"source sha256[:16]: `{src_hash}`",
+           f"- dispatch: `{kname}`, grid {big} threads",
+           f"- timed steps (last {steps_kt} d-cache verify dispatches of the kernel-trace run): "
+           f"average {dur.mean():.1f} us, min {dur.min():.1f} us, max {dur.max():.1f} us\n",
+           "## --kernel-trace --stats (all dispatches of the run)\n",
+           "| kernel | calls | average us | total ms | % |", "|---|---|---|---|---|"]
+    for r in stats[:8]:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) * 1e-3:.1f} | "
+                   f"{float(r['TotalDurationNs']) * 1e-6:.2f} | {float(r['Percentage']):.1f} |")
+    out.append("\nThe d-cache line's stats average includes the ring pre-fill calls with one-token "
+               "windows; the timed-step average above is the figure to use.\n")
+    out.append("## HBM bytes (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)\n")
+    out.append("| | FETCH_SIZE KiB | WRITE_SIZE KiB |")
+    out.append("|---|---|---|")
+    out.append(f"| dcache_verify_kernel, mean of the last {steps_pmc} dispatches | {fv:.0f} | {wv:.0f} |")
+    out.append(f"| plain copy of {COPY_BYTES >> 20} MiB (mean of 3) | {fc:.0f} | {wc:.0f} |")
+    out.append(f"\nScale factors (copy bytes / counter): fetch {f_fetch:.4f}, write {f_write:.4f}.\n")
+    out.append(f"HBM bytes per launch (scaled): {hbm:.4e} (fetch {fv * f_fetch * 1024:.4e}, "
+               f"write {wv * f_write * 1024:.4e})")
+    if alg:
+        out.append(f"\nAlgorithmic bytes per launch (bench.py `dcache_alg_bytes`): {alg:.4e}; "
+                   f"{alg / t / 1e9:.0f} GB/s at the timed average, {alg / t / 1e9 / 8000.0:.3f} of 8 TB/s; "
+                   f"counter / algorithmic = {hbm / alg:.3f}.")
+    rows = _csv(os.path.join(d, "alu", "run_counter_collection.csv"))
+
+    def cval(name):
+        g = max(int(r["Grid_Size"]) for r in rows if is_dc(r))
+        v = [float(r["Counter_Value"]) for r in rows
+             if r["Counter_Name"] == name and is_dc(r) and int(r["Grid_Size"]) == g][-steps_pmc:]
+        return float(np.mean(v)) if v else float("nan")
+
+    valu, salu, lds = cval("SQ_INSTS_VALU"), cval("SQ_INSTS_SALU"), cval("SQ_INSTS_LDS")
+    waves, wcyc, wissue, wany, gui = (cval("SQ_WAVES"), cval("SQ_WAVE_CYCLES"), cval("SQ_WAIT_INST_ANY"),
+                                      cval("SQ_WAIT_ANY"), cval("GRBM_GUI_ACTIVE"))
+    clock = gui / XCDS / t
+    issue = valu * 4 / SIMDS / clock
+    out.append(f"\n## Instructions and wave states per launch (--pmc, mean of the last {steps_pmc} "
+               "dispatches)\n")
+    out.append("| SQ_INSTS_VALU | SQ_INSTS_SALU | SQ_INSTS_LDS | SQ_WAVES | GRBM_GUI_ACTIVE |")
+    out.append("|---|---|---|---|---|")
+    out.append(f"| {valu:.4e} | {salu:.4e} | {lds:.4e} | {waves:.0f} | {gui:.4e} |")
+    out.append(f"\nPer wave: {valu / waves:.0f} VALU, {salu / waves:.0f} SALU and {lds / waves:.0f} LDS "
+               f"instructions. Clock over the timed average: GRBM_GUI_ACTIVE / {XCDS} dies / "
+               f"{dur.mean():.1f} us = {clock / 1e9:.2f} GHz. VALU issue time (SQ_INSTS_VALU x 4 cycles / "
+               f"{SIMDS} SIMDs / clock) = {issue * 1e6:.1f} us, {100.0 * issue / t:.0f}% of the kernel's time.")
+    out.append(f"Of the waves' cycles (SQ_WAVE_CYCLES), {100.0 * wissue / wcyc:.0f}% were spent ready but "
+               f"waiting for an issue slot (SQ_WAIT_INST_ANY) and {100.0 * wany / wcyc:.0f}% waiting on "
+               "loads, LDS or barriers (SQ_WAIT_ANY).")
+    os.makedirs(os.path.dirname(DCACHE_PROFILE_SUMMARY), exist_ok=True)
+    with open(DCACHE_PROFILE_SUMMARY, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
