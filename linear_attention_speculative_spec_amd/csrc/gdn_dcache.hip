@@ -34,8 +34,8 @@
 //      that share a column) and its key rows, and forms their dot products on
 //      MFMA 16x16x32 bf16: raw bf16 keys give exact products summed in fp32
 //      (fp32 activations enter as bf16 high parts plus remainders, three
-//      products per step); wave 0 writes the normalised window columns to
-//      LDS and the window keys to the raw ring, the last wave forms the gates
+//      products per step); one wave writes the normalised window columns to
+//      LDS and the window keys to the raw ring, another forms the gates
 //      and their prefix sums (DPP scan);
 //   3. (barrier) the coupling and output coefficients, over all threads;
 //   4. (barrier) each wave: S0 [kh_w, qh_w] for its 16 rows on MFMA 4x4x1
@@ -72,7 +72,13 @@ struct DcCfg {
     static constexpr int eb = Act::bytes;
     static constexpr bool kF32 = eb == 4;
     static constexpr int KS = K / 32;              // matrix steps over the key
-    static constexpr int NCT = (2 * TM + 15) / 16; // 16-column groups of window columns
+    static constexpr int TP = TM;                  // window columns of each kind (keys, queries)
+    static constexpr int PC = 2 * TP;              // window columns: keys 0..TP-1, queries TP..
+    static constexpr int NCT = (PC + 15) / 16;     // 16-column groups of window columns
+    static constexpr int SW = PC + 16 * NCT + 4;   // row stride of a wave's result rows
+    static constexpr int CPC = K * eb / 16;        // 16-byte chunks of a key row
+    static constexpr int NBL = (2 * TM * CPC + kDcThreads - 1) / kDcThreads;   // window chunks per thread
+    static constexpr int BRS = K * eb + 16;        // bytes per raw window column in LDS (16-byte pad: banks)
     static constexpr int RPL = LM / 64;            // gate records per lane
     static constexpr int NTW = LM / 64;            // 16-record key tiles per wave
     // registers: checkpoint tile, deltas, window values, window and key
@@ -88,7 +94,7 @@ struct DcCfg {
 };
 
 struct DcParams {
-    int B, T, TP, PC, H, HV, V, L, num_slots, write_ring, nparts, nunits;
+    int B, T, H, HV, V, L, num_slots, write_ring, nparts, nunits;
     float scale, softplus_threshold, eps;
     const void *q, *k, *v, *a, *b;
     const float *A_log, *dt_bias;
@@ -102,10 +108,15 @@ struct DcParams {
     float* rd;
     void* o;
     // the workgroup's LDS, in floats: X [PC][KX] normalised window keys
-    // (columns 0..TP-1) and queries (TP..2TP-1); P [L][PC] dot products,
-    // then coefficients; gam [L], bet [L]; SP [kDcWaves][PC][16] each wave's
-    // S0 products
-    int KX, o_p, o_gam, o_bet, o_sp;
+    // (columns 0..TP-1) and queries (TP..PC-1); P [L + 4][PC] raw dot
+    // products, then the history's coefficients (rows hist .. hist + 2
+    // zero); W [TP][PC] the window records' coefficients; E [PC] the window
+    // tokens' decays e^{Gam}; BW [TP] their betas; RNC [PC] window column
+    // norms; gam [L], bet [L], RN [L] records' prefix gates (log2), betas,
+    // key norms; R [kDcWaves][16][SW] each wave's rows: decayed S0 products
+    // (columns 0..PC-1), then the history's sums (PC..); BR [16 NCT] raw
+    // window columns (keys 0..T-1, then queries), the dot products' operands
+    int KX, o_p, o_w, o_e, o_bw, o_rnc, o_gam, o_bet, o_rn, o_r, o_br;
 };
 
 // Read-only, wave-uniform metadata through the constant address space.
@@ -140,11 +151,48 @@ __device__ __forceinline__ float quarters_sum_dc(float x)
     return swap32_sum_dc(swap16_sum_dc(x));
 }
 
-// Sum over the eight lanes l % 8 + 8 c (c = 0..7), delivered to each.
-__device__ __forceinline__ float rows8_sum_dc(float x)
+// Sum over aligned groups of N lanes (N = 8, 16, 32 or 64), delivered to
+// each lane of the group: DPP within quads, half rows and rows, then lane
+// swaps between rows.
+template <int N>
+__device__ __forceinline__ float group_sum_dc(float x)
 {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-    return quarters_sum_dc(x);
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group of 8, 16, 32 or 64 lanes");
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));   // row_half_mirror
+    if constexpr (N >= 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));   // row_mirror
+    if constexpr (N >= 32)
+        x = swap16_sum_dc(x);
+    if constexpr (N >= 64)
+        x = swap32_sum_dc(x);
+    return x;
+}
+
+// Two values summed over lane pairs at once: lanes with bit 5 clear (lanes
+// 0..31) receive x[l] + x[l ^ 32], the others y[l] + y[l ^ 32].
+__device__ __forceinline__ float pair32_sum(float x, float y)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const unsigned a = p[0], b = p[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+
+// The same over lane bit 4: x[l] + x[l ^ 16] where bit 4 is clear, else
+// y[l] + y[l ^ 16].
+__device__ __forceinline__ float pair16_sum(float x, float y)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const unsigned a = p[0], b = p[1];
+    return __uint_as_float(a) + __uint_as_float(b);
+}
+
+// The same over lane bit 3 (a DPP rotation by 8 within each 16-lane row).
+__device__ __forceinline__ float pair8_sum(float x, float y, bool b3)
+{
+    const float send = b3 ? x : y, keep = b3 ? y : x;
+    return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128, 0xF, 0xF, false));
 }
 
 // DPP move of x; lanes without a source receive 0.
@@ -188,27 +236,20 @@ __device__ __forceinline__ RawChunk<Act> load_raw(const typename Act::storage* r
 
 // The chunk as the operand of a bf16 matrix step: the raw bits themselves
 // (bf16), or the bf16 rounding hi and the bf16 rounding of the remainder lo
-// (fp32).  ss gains the values' sum of squares.  Dead lanes carry the values
-// of a valid row; their products and norms are never stored.
+// (fp32).  Dead lanes carry the values of a valid row; their products are
+// never stored.
 template <class Act>
 struct KeyChunk {
     bf16x8 hi, lo;
 };
 
 template <class Act>
-__device__ __forceinline__ KeyChunk<Act> to_operand(const RawChunk<Act>& r, float& ss)
+__device__ __forceinline__ KeyChunk<Act> to_operand(const RawChunk<Act>& r)
 {
     KeyChunk<Act> c;
     if constexpr (Act::bytes == 2) {
-        const uint4 w = r.w[0];
-        c.hi = __builtin_bit_cast(bf16x8, w);
+        c.hi = __builtin_bit_cast(bf16x8, r.w[0]);
         c.lo = c.hi;
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16x2 x = __builtin_bit_cast(bf16x2, u[e]);
-            ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
-        }
     } else {
         const uint4 w0 = r.w[0], w1 = r.w[1];
         const float x[8] = {__uint_as_float(w0.x), __uint_as_float(w0.y), __uint_as_float(w0.z), __uint_as_float(w0.w),
@@ -218,13 +259,36 @@ __device__ __forceinline__ KeyChunk<Act> to_operand(const RawChunk<Act>& r, floa
         for (int e = 0; e < 4; ++e) {
             h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
             l[e] = pack_bf16x2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
-            ss = __builtin_fmaf(x[2 * e], x[2 * e], ss);
-            ss = __builtin_fmaf(x[2 * e + 1], x[2 * e + 1], ss);
         }
         c.hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
         c.lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
     }
     return c;
+}
+
+// ss plus the chunk's sum of squares (of the activations as stored).
+template <class Act>
+__device__ __forceinline__ float raw_sumsq(const RawChunk<Act>& r, float ss)
+{
+    if constexpr (Act::bytes == 2) {
+        const uint4 w = r.w[0];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 x = __builtin_bit_cast(bf16x2, u[e]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 w = r.w[h];
+            const float x[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ss = __builtin_fmaf(x[e], x[e], ss);
+        }
+    }
+    return ss;
 }
 
 // The chunk's eight values as fp32 (exact for bf16; hi + lo for fp32).
@@ -285,20 +349,23 @@ __device__ __forceinline__ void load_tile(const float* rows, int lane, f32x4 (&s
 
 // Stored deltas of lane (row l % 16, group l / 16): records grp + 4 m, m <
 // kDPre.  Every load is issued (records past the history read the last one,
-// or record 0, again; their values are never used): loads under a branch
+// or record 0, again; their coefficients are zero): loads under a branch
 // would turn the array into one register vector copied by every branch.
+// Offsets are 32-bit from the slab's (uniform) address.
 __device__ __forceinline__ void load_deltas(const float* slab, int V, int L, int base, int hist, int lane,
                                             float (&d)[kDPre])
 {
-    const int grp = lane >> 4;
-    const uint32_t off = static_cast<uint32_t>((lane & 15) * 4);
-    const int hl = hist > 0 ? hist - 1 : 0;
+    const char* sb = reinterpret_cast<const char*>(slab);
+    const uint32_t rb = static_cast<uint32_t>(V) * 4u;
+    const uint32_t l4 = static_cast<uint32_t>(lane & 15) * 4u;
+    const uint32_t wrap = static_cast<uint32_t>(L - 1);
+    const int hb = base + (hist > 0 ? hist - 1 : 0);   // the last history record, before the wrap
+    const int gb = base + (lane >> 4);
 #pragma unroll
     for (int m = 0; m < kDPre; ++m) {
-        const int j = grp + 4 * m;
-        const int jc = j < hl ? j : hl;
-        const char* row = reinterpret_cast<const char*>(slab + static_cast<size_t>((base + jc) & (L - 1)) * V);
-        d[m] = *reinterpret_cast<const float*>(row + off);
+        const int jb = gb + 4 * m;
+        const uint32_t ph = static_cast<uint32_t>(jb < hb ? jb : hb) & wrap;
+        d[m] = *reinterpret_cast<const float*>(sb + (__umul24(ph, rb) + l4));
     }
 }
 
@@ -332,37 +399,38 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
     const int T = p.T, H = p.H;
     const st* kin = static_cast<const st*>(p.k);
     const st* qin = static_cast<const st*>(p.q);
-    // ---- 1. loads.  The window columns first: they depend on the row and
-    // qk head only, so they are in flight while the slot's cursors are read.
-    // Column c = 16 ct + l % 16 (keys 0..T-1, then queries), key elements
-    // 32 ks + 8 (l / 16) .. +7; dead columns read window key 0.
-    RawChunk<Act> bcol_raw[NCT][KS];
+    // ---- 1. loads.  The window columns first, once per workgroup: they
+    // depend on the row and qk head only, so they are in flight while the
+    // slot's cursors are read.  Chunk m of thread tid: live column c = idx /
+    // CPC (keys 0..T-1, then queries), bytes 16 (idx % CPC) .. +15, idx = tid
+    // + 256 m; threads past the live columns read column 0 again.
+    constexpr int CPC = Cfg::CPC, NBL = Cfg::NBL;
+    uint4 braw[NBL];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int c = 16 * ct + rl;
+    for (int m = 0; m < NBL; ++m) {
+        const int idx = tid + kDcThreads * m;
+        const int c = idx / CPC, e = idx % CPC;
         const bool live = c < 2 * T;
         const bool isq = live && c >= T;
         const int t = live ? (isq ? c - T : c) : 0;
         const st* row = (isq ? qin : kin) + ((static_cast<size_t>(b) * T + t) * H + h) * K;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bcol_raw[ct][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
+        braw[m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(row) + 16 * e);
     }
     const int s = ldu(p.slot_idx, b);
     if (!valid_slot(s, p.num_slots)) {
         // padding row: nothing written (the window columns in flight count as used)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int e = 0; e < (Cfg::eb == 2 ? 1 : 2); ++e)
-                    asm volatile("" ::"v"(bcol_raw[ct][ks].w[e].x), "v"(bcol_raw[ct][ks].w[e].y),
-                                 "v"(bcol_raw[ct][ks].w[e].z), "v"(bcol_raw[ct][ks].w[e].w));
+        for (int m = 0; m < NBL; ++m)
+            asm volatile("" ::"v"(braw[m].x), "v"(braw[m].y), "v"(braw[m].z), "v"(braw[m].w));
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int TP = p.TP, PC = p.PC, L = p.L, KX = p.KX, V = p.V, HV = p.HV;
+    // the wave with extra work (the gates) rotates with the workgroup number,
+    // so that no SIMD hosts all of them: the waves of a workgroup go to the
+    // SIMDs in order
+    const int gwave = static_cast<int>(blockIdx.x >> 3) & 3;
+    constexpr int TP = Cfg::TP, PC = Cfg::PC, SW = Cfg::SW;
+    const int L = p.L, KX = p.KX, V = p.V, HV = p.HV;
     const bool flagged = ldu(p.is_flush, s) != 0;
     const int wpc = clamp_wp(ldu(p.write_pos, s), L, T);
     const int base = ldu(p.cache_base, s);
@@ -378,25 +446,29 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
     st* ringk = static_cast<st*>(p.rawk) + (static_cast<size_t>(s) * H + h) * L * K;
 
     // then this wave's key tiles, gate inputs, window values and deltas
+    // (tiles past the last record load nothing: their products are never
+    // formed)
     RawChunk<Act> arow_raw[NTW][KS];
 #pragma unroll
     for (int tw = 0; tw < NTW; ++tw) {
-        const int j = 16 * (wave + kDcWaves * tw) + rl;
-        const bool live = j < n;
-        // dead lanes read window key 0 (valid memory; dropped below)
-        const st* row = (live && j < hist) ? ringk + static_cast<size_t>((base + j) & (L - 1)) * K
-                                           : kin + ((static_cast<size_t>(b) * T + (live ? j - hist : 0)) * H + h) * K;
+        if (16 * (wave + kDcWaves * tw) < n) {
+            const int j = 16 * (wave + kDcWaves * tw) + rl;
+            const bool live = j < n;
+            // dead lanes read window key 0 (valid memory; dropped below)
+            const st* row = (live && j < hist) ? ringk + static_cast<size_t>((base + j) & (L - 1)) * K
+                                               : kin + ((static_cast<size_t>(b) * T + (live ? j - hist : 0)) * H + h) * K;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            arow_raw[tw][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
+            for (int ks = 0; ks < KS; ++ks)
+                arow_raw[tw][ks] = load_raw<Act>(row, 32 * ks + 8 * grp);
+        }
     }
-    // gate inputs of records RPL lane + q (last wave): raw bits of the ring's
+    // gate inputs of records RPL lane + q (gate wave): raw bits of the ring's
     // g and beta, or of the window's a and b (widened in step 2)
     constexpr int RPL = Cfg::RPL;
     typedef typename std::conditional<Cfg::eb == 2, uint16_t, uint32_t>::type actraw;
     uint32_t ga[RPL], gb[RPL];
     const size_t gslab = head * L;
-    if (wave == kDcWaves - 1) {
+    if (wave == gwave) {
 #pragma unroll
         for (int q = 0; q < RPL; ++q) {
             const int j = RPL * lane + q;
@@ -422,49 +494,70 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
     float dpre[kDPre];
     load_deltas(p.rd + head * L * V + r0, V, L, base, hist, lane, dpre);
 
-    // ---- 2. norms and dot products; X (wave 0); gates and prefix sums (last wave)
-    KeyChunk<Act> bcol[NCT][KS];
-    float rnc[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const bool live = 16 * ct + rl < 2 * T;
-        float ss = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bcol[ct][ks] = to_operand<Act>(bcol_raw[ct][ks], ss);
-        ss = quarters_sum_dc(ss);
-        rnc[ct] = live ? __builtin_amdgcn_rsqf(ss + p.eps) : 0.0f;
-    }
-    if (wave == 0) {
+    // ---- 2. dot products of this wave's key rows and the window columns;
+    // norms; X (one wave); gates and prefix sums (another)
+    float* W = sm + p.o_w;
+    float* E = sm + p.o_e;
+    float* BW = sm + p.o_bw;
+    float* RNC = sm + p.o_rnc;
+    float* RN = sm + p.o_rn;
+    char* BR = reinterpret_cast<char*>(sm + p.o_br);
+    {
+        // the window columns: raw bits to BR, normalised to X (norms reduced
+        // over the CPC threads of a column), the keys to the ring (part 0 of
+        // the first value head of the qk head); dead rows of X are zero
         const bool k_writer = wr && (hv % G == 0) && part == 0;
+        constexpr int EPC = 16 / Cfg::eb;            // elements per chunk
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int c = 16 * ct + rl;
+        for (int m = 0; m < NBL; ++m) {
+            const int idx = tid + kDcThreads * m;
+            const int c = idx / CPC, e = idx % CPC;
+            const uint4 w = braw[m];
+            float x[EPC];
+            if constexpr (Cfg::eb == 2) {
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    x[2 * q] = __uint_as_float(u[q] << 16);
+                    x[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+                }
+            } else {
+                x[0] = __uint_as_float(w.x);
+                x[1] = __uint_as_float(w.y);
+                x[2] = __uint_as_float(w.z);
+                x[3] = __uint_as_float(w.w);
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int q = 0; q < EPC; ++q)
+                ss = __builtin_fmaf(x[q], x[q], ss);
+            ss = group_sum_dc<CPC>(ss);
             if (c < 2 * T) {
                 const bool isq = c >= T;
                 const int t = isq ? c - T : c;
-                float* xc = X + (isq ? TP + t : t) * KX;
-                const float rn = rnc[ct];
+                const int col = isq ? TP + t : t;
+                const float rn = __builtin_amdgcn_rsqf(ss + p.eps);
+                *reinterpret_cast<uint4*>(BR + c * Cfg::BRS + 16 * e) = w;
+                float* dst = X + col * KX + EPC * e;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    float x[8];
-                    chunk_values<Act>(bcol[ct][ks], x);
-                    float* dst = xc + 32 * ks + 8 * grp;
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{x[0] * rn, x[1] * rn, x[2] * rn, x[3] * rn};
-                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{x[4] * rn, x[5] * rn, x[6] * rn, x[7] * rn};
-                    if (!isq && k_writer)
-                        store_raw<Act>(ringk + static_cast<size_t>((wp0 + t) & (L - 1)) * K + 32 * ks + 8 * grp,
-                                       bcol_raw[ct][ks]);
-                }
+                for (int q = 0; q < EPC; q += 4)
+                    *reinterpret_cast<f32x4*>(dst + q) = f32x4{x[q] * rn, x[q + 1] * rn, x[q + 2] * rn, x[q + 3] * rn};
+                if (!isq && k_writer)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ringk + static_cast<size_t>((wp0 + t) & (L - 1)) * K) + 16 * e) = w;
+                if (e == 0)
+                    RNC[col] = rn;
+            } else if (c < 2 * TP) {
+                // window columns T..TP-1 and TP+T..PC-1 are zero (their products are never read)
+                const int z = c - 2 * T;
+                const int col = z < TP - T ? T + z : TP + T + (z - (TP - T));
+                float* dst = X + col * KX + EPC * e;
+#pragma unroll
+                for (int q = 0; q < EPC; q += 4)
+                    *reinterpret_cast<f32x4*>(dst + q) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
-        // window columns T..TP-1 and TP+T..2TP-1 are zero (their products are never read)
-        for (int e = lane; e < 2 * (TP - T) * K; e += 64) {
-            const int zc = e / K, kk = e % K;
-            X[(zc < TP - T ? T + zc : TP + T + (zc - (TP - T))) * KX + kk] = 0.0f;
-        }
     }
-    if (wave == kDcWaves - 1) {
+    if (wave == gwave) {
         // gates of the combined sequence: history as recorded, window formed
         // here (and recorded in the ring by part 0); prefix sums
         float gl[RPL], bl[RPL];
@@ -500,22 +593,40 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             }
         }
     }
-    // this wave's key tiles against the window columns; lane l, register q:
-    // record 16 (wave + 4 tw) + 4 (l / 16) + q, column 16 ct + l % 16
+    __syncthreads();
+    // the window columns as operands of the bf16 matrix steps (column 16 ct +
+    // l % 16, key elements 32 ks + 8 (l / 16) .. +7; columns past 2T hold
+    // whatever LDS held: their products are never stored)
+    KeyChunk<Act> bcol[NCT][KS];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const char* src = BR + (16 * ct + rl) * Cfg::BRS + (32 * ks + 8 * grp) * Cfg::eb;
+            RawChunk<Act> rc;
+            rc.w[0] = *reinterpret_cast<const uint4*>(src);
+            if constexpr (Cfg::eb == 4)
+                rc.w[1] = *reinterpret_cast<const uint4*>(src + 16);
+            bcol[ct][ks] = to_operand<Act>(rc);
+        }
+    // this wave's key tiles against the window columns (raw products, the
+    // norms enter with the coefficients); lane l, register q: record 16
+    // (wave + 4 tw) + 4 (l / 16) + q, column 16 ct + l % 16
 #pragma unroll
     for (int tw = 0; tw < NTW; ++tw) {
         const int j0 = 16 * (wave + kDcWaves * tw);
-        const bool live = j0 + rl < n;
+        if (j0 >= n)
+            continue;
         KeyChunk<Act> arow[KS];
         float ss = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            arow[ks] = to_operand<Act>(arow_raw[tw][ks], ss);
-        const float rnj = live ? __builtin_amdgcn_rsqf(quarters_sum_dc(ss) + p.eps) : 0.0f;
-        float rnr[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            rnr[q] = __shfl(rnj, 4 * grp + q, 64);
+        for (int ks = 0; ks < KS; ++ks) {
+            arow[ks] = to_operand<Act>(arow_raw[tw][ks]);
+            ss = raw_sumsq<Act>(arow_raw[tw][ks], ss);
+        }
+        ss = quarters_sum_dc(ss);
+        if (grp == 0 && j0 + rl < n)
+            RN[j0 + rl] = __builtin_amdgcn_rsqf(ss + p.eps);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -529,7 +640,7 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
                 for (int q = 0; q < 4; ++q) {
                     const int jr = j0 + 4 * grp + q;
                     if (jr < n)
-                        P[jr * PC + col] = acc[q] * rnr[q] * rnc[ct];
+                        P[jr * PC + col] = acc[q];
                 }
             }
         }
@@ -543,20 +654,41 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
 
     // ---- 3. coefficients: column i < T of record j couples window token i to
     // j (j < hist + i): beta e^{Gam_{h+i} - Gam_j} kh_i . kh_j; query column t
-    // weighs d_j in output t (j <= hist + t): e^{Gam_{h+t} - Gam_j} kh_j . qh_t
-    for (int task = tid; task < n * PC; task += kDcThreads) {
-        const int j = task / PC, col = task - j * PC;
-        const bool isq = col >= TP;
-        const int t = isq ? col - TP : col;
-        float coef = 0.0f;
-        if (t < T) {
-            const int i = hist + t;
-            if (isq ? j <= i : j < i) {
-                const float w = __builtin_amdgcn_exp2f(gam[i] - gam[j]);
-                coef = (isq ? w : bet[i] * w) * P[task];
+    // weighs d_j in output t (j <= hist + t): e^{Gam_{h+t} - Gam_j} kh_j . qh_t.
+    // History records' coefficients stay in P, whose rows hist .. hist + 2
+    // become zero (the history product reads them for records past the
+    // history); the window records' go to W.
+    {
+        const int nz = hist + (T > 3 ? T : 3);
+        for (int task = tid; task < nz * PC; task += kDcThreads) {
+            const int j = task / PC, col = task % PC;
+            const bool isq = col >= TP;
+            const int t = isq ? col - TP : col;
+            float coef = 0.0f;
+            if (j < n && t < T) {
+                const int i = hist + t;
+                if (isq ? j <= i : j < i) {
+                    const float w = __builtin_amdgcn_exp2f(gam[i] - gam[j]);
+                    coef = (isq ? w : bet[i] * w) * (P[task] * (RN[j] * RNC[col]));
+                }
+            }
+            if (j < hist) {
+                P[task] = coef;
+            } else {
+                P[task] = 0.0f;
+                if (j < n)
+                    W[(j - hist) * PC + col] = coef;
             }
         }
-        P[task] = coef;
+        if (tid < PC) {
+            const bool isq = tid >= TP;
+            const int t = isq ? tid - TP : tid;
+            E[tid] = t < T ? __builtin_amdgcn_exp2f(gam[hist + t]) : 0.0f;
+            for (int u = T; u < TP; ++u)
+                W[u * PC + tid] = 0.0f;
+            if (tid < TP)
+                BW[tid] = tid < T ? bet[hist + tid] : 0.0f;
+        }
     }
     __syncthreads();
 
@@ -570,57 +702,63 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             asm volatile("" ::"v"(dpre[m]));
         return;
     }
-    float* SPl = sm + p.o_sp + wave * PC * 16;
-    // S0 [kh_w, qh_w] for the tile's rows, four columns per group; lane l,
-    // register q of the sums: column 4 cg + q of row 8 hh + l % 8 (hh = 0:
-    // even loads, 1: odd), partial over key group l / 8
-    for (int cg = 0; cg < PC / 4; ++cg) {
-        const float* xrow = X + (4 * cg + (lane & 3)) * KX + 4 * (lane >> 3);
-        f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0, b0 = a0, b1 = a0;
+    float* Rw = sm + p.o_r + wave * 16 * SW;
+    // e^{Gam} S0 [kh, qh] for the tile's rows, eight window columns at a time
+    // on MFMA 4x4x1: lane l, register q of acc[e][hh] holds column 8 cp + 4 e
+    // + q of row 8 hh + l % 8, partial over key group l / 8.  The 16 partial
+    // sums of a lane are reduced over the key groups (lane bits 3..5) while
+    // being spread out: afterwards lane l holds column 8 cp + l / 8 of rows
+    // l % 8 and 8 + l % 8.
+#pragma unroll
+    for (int cp = 0; cp < PC / 8; ++cp) {
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            acc[e][0] = acc[e][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < K / 16; ++i) {
-            const f32x4 za = *reinterpret_cast<const f32x4*>(xrow + 32 * (i >> 1));
-            if (i & 1) {
-                a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a1, 0, 0, 0);
-                b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b1, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a1, 0, 0, 0);
-                b1 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b1, 0, 0, 0);
-            } else {
-                a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[0], sraw[i][0], a0, 0, 0, 0);
-                b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[1], sraw[i][1], b0, 0, 0, 0);
-                a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[2], sraw[i][2], a0, 0, 0, 0);
-                b0 = __builtin_amdgcn_mfma_f32_4x4x1f32(za[3], sraw[i][3], b0, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const f32x4 za = *reinterpret_cast<const f32x4*>(
+                    X + (8 * cp + 4 * e + (lane & 3)) * KX + 4 * (lane >> 3) + 32 * (i >> 1));
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc[e][i & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(za[k], sraw[i][k], acc[e][i & 1], 0, 0, 0);
             }
         }
-        const f32x4 lo = a0 + b0, hi = a1 + b1;
-        const int c = lane >> 3;
-        float val = 0.0f;
+        float v8[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float sl = rows8_sum_dc(lo[q]), sh = rows8_sum_dc(hi[q]);
-            val = c == q ? sl : (c == 4 + q ? sh : val);
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v8[4 * hh + q] = pair32_sum(acc[0][hh][q], acc[1][hh][q]);
+        const bool b3 = (lane & 8) != 0;
+        const int c = 8 * cp + (lane >> 3);
+        const float ec = E[c];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float x = pair16_sum(v8[4 * hh], v8[4 * hh + 2]);
+            const float y = pair16_sum(v8[4 * hh + 1], v8[4 * hh + 3]);
+            Rw[(8 * hh + (lane & 7)) * SW + c] = pair8_sum(x, y, b3) * ec;
         }
-        SPl[(4 * cg + (c & 3)) * 16 + (lane & 7) + 8 * (c >> 2)] = val;
     }
-    // stored deltas against the coefficients: lane group grp takes records
-    // grp + 4 m of row rl; the four groups meet by lane swaps
-    float hA[TM], hF[TM];
+    // stored deltas against the history's coefficients on MFMA 16x16x4 f32:
+    // A (lane l) the delta of record grp + 4 m at row rl, B (lane l) the
+    // coefficient of record grp + 4 m in column 16 cb + rl; D (lane l,
+    // register r) row 4 grp + r, column 16 cb + rl.  Coefficient rows from
+    // hist on are zero, so records past the history weigh nothing (columns
+    // past PC read the next row and are never used).
+    f32x4 hacc[NCT];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        hA[t] = 0.0f;
-        hF[t] = 0.0f;
-    }
+    for (int cb = 0; cb < NCT; ++cb)
+        hacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < kDPre; ++m) {
-        const int j = grp + 4 * m;
-        if (4 * m < hist) {                      // uniform; records past hist weigh nothing
-            const float dj = j < hist ? dpre[m] : 0.0f;
-            const float* cj = P + (j < hist ? j : 0) * PC;
+        if (4 * m < hist) {                      // uniform
+            const float* cj = P + (grp + 4 * m) * PC + rl;
 #pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
-                hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
-            }
+            for (int cb = 0; cb < NCT; ++cb)
+                hacc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(dpre[m], cj[16 * cb], hacc[cb], 0, 0, 0);
         }
     }
     if constexpr (LM - 1 > 4 * kDPre) {
@@ -630,73 +768,68 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             const int j = grp + 4 * m;
             const int jc = j < hist ? j : hist - 1;
             const float dv = dslab[static_cast<size_t>((base + jc) & (L - 1)) * V];
-            const float dj = j < hist ? dv : 0.0f;
-            const float* cj = P + jc * PC;
+            const float* cj = P + j * PC + rl;
 #pragma unroll
-            for (int t = 0; t < TM; ++t) {
-                hA[t] = __builtin_fmaf(cj[t], dj, hA[t]);
-                hF[t] = __builtin_fmaf(cj[TP + t], dj, hF[t]);
-            }
+            for (int cb = 0; cb < NCT; ++cb)
+                hacc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(dv, cj[16 * cb], hacc[cb], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        hA[t] = quarters_sum_dc(hA[t]);
-        hF[t] = quarters_sum_dc(hF[t]);
-    }
+    for (int cb = 0; cb < NCT; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Rw[(4 * grp + r) * SW + PC + 16 * cb + rl] = hacc[cb][r];
     // window deltas of row r0 + rl: every lane forms all T of them (the
-    // recurrence); lane group grp then takes window positions and tokens
-    // t = grp + 4 m with uniform code (per-lane LDS indices and selects over
-    // the registers: one branch per token would be issued by every lane
-    // group), writing the output, the delta and the raw value
-    st* out = static_cast<st*>(p.o);
-    const int v = r0 + rl;
+    // recurrence); lane group grp then takes tokens t = grp + 4 m with
+    // uniform code (per-lane LDS indices and selects over the registers: one
+    // branch per token would be issued by every lane group), writing the
+    // output, the delta and the raw value
+    const float* Rr = Rw + rl * SW;
     float dw[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         dw[i] = 0.0f;
         if (i < T) {
-            const int ii = hist + i;
             float vi;
             if constexpr (Act::bytes == 2)
                 vi = bf16_to_f32(vw[i]);
             else
                 vi = vw[i];
-            float d = bet[ii] * (vi - __builtin_amdgcn_exp2f(gam[ii]) * SPl[i * 16 + rl]) - hA[i];
+            float d = BW[i] * (vi - Rr[i]) - Rr[PC + i];
 #pragma unroll
             for (int i2 = 0; i2 < TM; ++i2)
                 if (i2 < i)
-                    d = __builtin_fmaf(-P[(hist + i2) * PC + i], dw[i2], d);
+                    d = __builtin_fmaf(-W[i2 * PC + i], dw[i2], d);
             dw[i] = d;
         }
     }
+    char* obase = reinterpret_cast<char*>(static_cast<st*>(p.o) + (static_cast<size_t>(b) * T * HV + hv) * V + r0);
+    char* dbase = reinterpret_cast<char*>(p.rd + gslab * V + r0);
+    char* vbase = reinterpret_cast<char*>(static_cast<st*>(p.rawv) + gslab * V + r0);
 #pragma unroll
-    for (int m = 0; m < (TM + 3) / 4; ++m) {
+    for (int m = 0; m < TM / 4; ++m) {
         const int t = grp + 4 * m;
         const int tc = t < T ? t : T - 1;          // dead lanes read a valid token
-        const int i = hist + tc;
-        float hsel = 0.0f, dsel = 0.0f;
+        float dsel = 0.0f;
         st vsel = vw[0];
 #pragma unroll
         for (int u = 0; u < TM; ++u) {
-            hsel = tc == u ? hF[u] : hsel;
             dsel = tc == u ? dw[u] : dsel;
             vsel = tc == u ? vw[u] : vsel;
         }
-        float acc = __builtin_amdgcn_exp2f(gam[i]) * SPl[(TP + tc) * 16 + rl] + hsel;
+        float acc = Rr[TP + tc] + Rr[PC + TP + tc];
+        const float* wq = W + TP + tc;
 #pragma unroll
-        for (int u = 0; u < TM; ++u) {
-            const int ju = hist + u < n ? hist + u : n - 1;
-            const float f = __builtin_fmaf(P[ju * PC + TP + tc], dw[u], acc);
-            acc = u <= tc ? f : acc;
-        }
+        for (int u = 0; u < TM; ++u)
+            if (u < T)                             // coefficients past token tc are zero
+                acc = __builtin_fmaf(wq[u * PC], dw[u], acc);
         if (t < T) {
-            const size_t tok = static_cast<size_t>(b) * T + t;
-            out[(tok * HV + hv) * V + v] = Act::from_f32(p.scale * acc);
+            const uint32_t oo = static_cast<uint32_t>(t * HV * V + rl) * Cfg::eb;
+            *reinterpret_cast<st*>(obase + oo) = Act::from_f32(p.scale * acc);
             if (wr) {
-                const size_t ri = (gslab + ((wp0 + t) & (L - 1))) * V + v;
-                p.rd[ri] = dsel;
-                static_cast<st*>(p.rawv)[ri] = vsel;
+                const uint32_t ri = static_cast<uint32_t>(((wp0 + t) & (L - 1)) * V + rl);
+                *reinterpret_cast<float*>(dbase + ri * 4u) = dsel;
+                *reinterpret_cast<st*>(vbase + ri * Cfg::eb) = vsel;
             }
         }
     }
@@ -707,20 +840,34 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
 namespace {
 
 struct DcLayout {
-    int TP, PC, KX, o_p, o_gam, o_bet, o_sp, total;   // floats
+    int KX, o_p, o_w, o_e, o_bw, o_rnc, o_gam, o_bet, o_rn, o_r, o_br, total;   // floats
 };
+
+// Window capacity of the instantiation that serves T tokens.
+int dc_tm(int T)
+{
+    return T <= 4 ? 4 : (T <= 8 ? 8 : kTMax);
+}
 
 DcLayout dc_layout(const gdn_shape& sh)
 {
+    const int TP = dc_tm(sh.T), PC = 2 * TP;
+    const int SW = PC + 16 * ((PC + 15) / 16) + 4;
+    auto up4 = [](int x) { return (x + 3) & ~3; };
     DcLayout d;
-    d.TP = (sh.T + 3) & ~3;
-    d.PC = 2 * d.TP;
     d.KX = sh.K + 16;   // rows read four at a time as 16-byte groups: a 64-byte pad keeps them off each other's banks
-    d.o_p = d.PC * d.KX;
-    d.o_gam = d.o_p + sh.L * d.PC;
+    d.o_p = PC * d.KX;
+    d.o_w = d.o_p + (sh.L + 4) * PC;
+    d.o_e = d.o_w + TP * PC;
+    d.o_bw = d.o_e + PC;
+    d.o_rnc = up4(d.o_bw + TP);
+    d.o_gam = d.o_rnc + PC;
     d.o_bet = d.o_gam + sh.L;
-    d.o_sp = (d.o_bet + sh.L + 3) & ~3;
-    d.total = d.o_sp + kDcWaves * d.PC * 16;
+    d.o_rn = d.o_bet + sh.L;
+    d.o_r = up4(d.o_rn + sh.L);
+    d.o_br = d.o_r + kDcWaves * 16 * SW;
+    const int brs = sh.K * (sh.act == GDN_BF16 ? 2 : 4) + 16;   // bytes per raw window column
+    d.total = d.o_br + 16 * ((PC + 15) / 16) * brs / 4;
     return d;
 }
 
@@ -787,8 +934,6 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
     DcParams p = {};
     p.B = sh.B;
     p.T = sh.T;
-    p.TP = lay.TP;
-    p.PC = lay.PC;
     p.H = sh.H;
     p.HV = sh.HV;
     p.V = sh.V;
@@ -820,9 +965,15 @@ hipError_t launch_dcache_verify(const gdn_shape& sh, const WindowPtrs& w, const 
     p.o = o;
     p.KX = lay.KX;
     p.o_p = lay.o_p;
+    p.o_w = lay.o_w;
+    p.o_e = lay.o_e;
+    p.o_bw = lay.o_bw;
+    p.o_rnc = lay.o_rnc;
     p.o_gam = lay.o_gam;
     p.o_bet = lay.o_bet;
-    p.o_sp = lay.o_sp;
+    p.o_rn = lay.o_rn;
+    p.o_r = lay.o_r;
+    p.o_br = lay.o_br;
     return sh.act == GDN_BF16 ? launch_dc_act<ActBF16>(sh, p, stream)
                               : launch_dc_act<ActF32>(sh, p, stream);
 }
