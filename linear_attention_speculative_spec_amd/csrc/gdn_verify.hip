@@ -368,6 +368,15 @@ __device__ __forceinline__ void load_item_cursors(KParams& p, Item& c)
 
 // The item after c in this workgroup's sequence: add the grid stride digit by
 // digit (no integer division per item).  Past the end the item is repeated.
+// The waves with extra work (the gates; the Z units) move by two waves in
+// the second half of the grid.  Two workgroups share a compute unit, one
+// from each half, and the waves of a workgroup go to the SIMDs in order, so
+// the two workgroups put that work on different SIMDs.
+__device__ __forceinline__ int role_shift()
+{
+    return 2 * blockIdx.x >= gridDim.x ? 2 : 0;
+}
+
 __device__ __forceinline__ Item next_item(KParams& p, const Item& c)
 {
     Item d = c;
@@ -431,11 +440,11 @@ __device__ __forceinline__ void issue_prefetch(KParams& p, const Item& c, int ti
             f.xw[m] = ld16(isq ? qwin : kwin, off);
         }
     }
-    // gate inputs of records RPL lane + r (the last wave forms the gates):
+    // gate inputs of records RPL lane + r (the gate wave forms the gates):
     // every lane loads all four, at clamped in-range indices, so no load is
     // conditional (a register written by a load on one path and a copy on
     // the other would have to wait for the load)
-    if (wave == kWaves - 1) {
+    if (wave == kWaves - 1 - role_shift()) {
         const size_t gbase = (static_cast<size_t>(c.s) * HV + c.hv) * L;
         const int hl = hist > 0 ? hist - 1 : 0;
 #pragma unroll
@@ -656,7 +665,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
     // queries (fp32 activations: bf16 hi + lo), their l2 norms reduced from
     // the same registers, zero padding rows, the window's ring records
     // (pre-mutation raw bits, single writer per qk head), and the gates with
-    // their prefix sums (last wave).  It runs while the previous item's
+    // their prefix sums (gate wave).  It runs while the previous item's
     // outputs are formed: X, the norms and the gates are not read by that
     // phase.
     auto stage_keys = [&](const Item& c, const Prefetch<Cfg, Act>& pf, int tid, int lane, bool ring) {
@@ -713,8 +722,8 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 if (ch == 0)
                     rn[row] = 0.0f;
             }
-            // gates of the combined sequence and their prefix sums (last wave)
-            if (wave == kWaves - 1) {
+            // gates of the combined sequence and their prefix sums (gate wave)
+            if (wave == kWaves - 1 - role_shift()) {
                 const size_t gbase = (static_cast<size_t>(s) * pk2->HV + hv) * L;
                 float gl[Cfg::RPL], bl[Cfg::RPL];
                 float pair = 0.0f;
@@ -749,7 +758,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
                 }
             }
             // the gate registers count as consumed in every wave (only the
-            // last wave loaded them)
+            // gate wave loaded them)
 #pragma unroll
             for (int r = 0; r < Cfg::RPL; ++r)
                 asm volatile("" ::"v"(pf.rg[r]), "v"(pf.rb[r]), "v"(pf.ra[r]), "v"(pf.rbw[r]));
@@ -951,7 +960,8 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         __syncthreads();
         pk = launder(pk);
 
-        if (wave < (TP / 4) * (K / 64))
+        const int zwave = (wave + kWaves - role_shift()) & (kWaves - 1);
+        if (zwave < (TP / 4) * (K / 64))
             __builtin_amdgcn_s_setprio(2);
         else
             __builtin_amdgcn_s_setprio(0);
@@ -963,7 +973,7 @@ __global__ __launch_bounds__(kThreads, MINW) void verify_kernel(const VerifyPara
         constexpr int NKS = K / 64;
         constexpr int ZST = Cfg::ZST;
         const int nk8 = (n + 7) & ~7;          // rows n..nk8-1 are zero rows (< NQ0)
-        for (int u = wave; u < (TP / 4) * NKS; u += kWaves) {
+        for (int u = zwave; u < (TP / 4) * NKS; u += kWaves) {
             const int tg = u / NKS, ks = u % NKS;
             const float* crow = Cs + (4 * tg + (lane & 3)) * CST;
             const int kc = 64 * ks + lane;
