@@ -692,19 +692,19 @@ COPY_BYTES = 256 << 20
 PROFILE_CMDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/kt -o run --output-format csv -- "
-    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --no-fold-every-commit --no-dcache "
+    "python3 $R/bench.py --steps 50 --warmup 20 --no-cpu-baseline --no-snapshot --no-fold-every-commit --no-dcache --no-kda --no-chain "
     "--copy-calibration "
     "> $R/gpurun_out/prof/kt.log 2>&1",
     "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
-    "--no-dcache --copy-calibration",
+    "--no-dcache --no-kda --no-chain --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o run --output-format csv -- "
     "python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot --no-fold-every-commit "
-    "--no-dcache --copy-calibration",
+    "--no-dcache --no-kda --no-chain --copy-calibration",
     "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
     "SQ_INSTS_VALU_MFMA_BF16 SQ_INSTS_VALU_MFMA_F32 GRBM_GUI_ACTIVE -d $R/gpurun_out/prof/mfma -o run "
     "--output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-snapshot "
-    "--no-fold-every-commit --no-dcache",
+    "--no-fold-every-commit --no-dcache --no-kda --no-chain",
     "cd $R && python3 bench.py --summarize-profile gpurun_out/prof",
 ]
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA peaks of the part

@@ -25,24 +25,26 @@
 // Execution: one workgroup of four waves per item (row, value head, up to 64
 // value rows); wave w owns key tile w (records 16 w .. 16 w + 15, and 16 w +
 // 64 .. for 128-record rings) and value tile w (rows 16 w .. 16 w + 15):
-//   1. every load of the item is issued at once, the key side's first: the
-//      window keys and queries in the operand layout of the bf16 matrix
-//      instruction (16 columns x 32 key elements per step), the wave's key
-//      tile (ring history, then window keys), the gate inputs, the window
-//      values of the wave's rows, then its checkpoint rows and stored deltas;
-//   2. each wave normalises the window columns (norms reduced over the lanes
-//      that share a column) and its key rows, and forms their dot products on
-//      MFMA 16x16x32 bf16: raw bf16 keys give exact products summed in fp32
-//      (fp32 activations enter as bf16 high parts plus remainders, three
-//      products per step); one wave writes the normalised window columns to
-//      LDS and the window keys to the raw ring, another forms the gates
-//      and their prefix sums (DPP scan);
-//   3. (barrier) the coupling and output coefficients, over all threads;
-//   4. (barrier) each wave: S0 [kh_w, qh_w] for its 16 rows on MFMA 4x4x1
-//      straight from the checkpoint registers; the stored deltas meet the
-//      coefficients, four lane groups over the history, summed by lane
-//      swaps; each lane group runs the T-step window recurrence for the 16
-//      rows and writes every fourth output and delta.
+//   1. loads, the key side's first: the window keys and queries, once per
+//      workgroup (the threads share the live columns' 16-byte chunks), then
+//      each wave's key tile (ring history, then window keys; tiles past the
+//      last record load nothing) and the gate inputs, then the wave's
+//      checkpoint rows: waiting for the key side never waits for these;
+//   2. the window columns' norms (reduced over the threads of a column), their
+//      raw bits and normalised values to LDS, the window keys to the raw
+//      ring; one wave forms the gates and their prefix sums (DPP scan); after
+//      a barrier each wave forms the dot products of its key rows with the
+//      window columns on MFMA 16x16x32 bf16: raw bf16 keys give exact
+//      products summed in fp32 (fp32 activations enter as bf16 high parts
+//      plus remainders, three products per step); the stored deltas and the
+//      window values are issued;
+//   3. (barrier) the coupling and output coefficients, over all threads, with
+//      the key and column norms;
+//   4. (barrier) each wave: e^{Gam} S0 [kh, qh] for its 16 rows on MFMA 4x4x1
+//      straight from the checkpoint registers; the stored deltas against the
+//      history's coefficients on MFMA 16x16x4 f32; each lane group runs the
+//      T-step window recurrence for the 16 rows and writes every fourth
+//      output and delta.
 // Workgroups are not persistent: several items per compute unit are in
 // different phases at once, so one item's load latency is covered by the
 // others' arithmetic.  The items of one qk head (its value heads and value
@@ -86,10 +88,10 @@ struct DcCfg {
     static constexpr int kRegs = K / 4 + kDPre + TM + (kF32 ? 2 : 1) * 4 * KS * (NCT + NTW) + 36;
     // waves per SIMD: 6 (six workgroups per compute unit, 80 registers) for
     // bf16 windows of up to 4 tokens on 64-record rings up to K = 128: the
-    // checkpoint rows are loaded after the key operands are consumed, so the
-    // two never hold registers at once; else 4 where the estimate fits 128
-    // registers, else 2.  More items per compute unit cover more of each
-    // item's load latency.
+    // window columns take one 16-byte chunk per thread, and the deltas and
+    // window values are loaded once the key operands are consumed; else 4
+    // where the estimate fits 128 registers, else 2.  More items per compute
+    // unit cover more of each item's load latency.
     static constexpr int kMinWaves = (!kF32 && TM == 4 && LM == 64 && K <= 128) ? 6 : (kRegs <= 128 ? 4 : 2);
 };
 
@@ -484,15 +486,11 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             }
         }
     }
-    st vw[TM];
-    {
-        const st* vb = static_cast<const st*>(p.v) + (static_cast<size_t>(b) * T * HV + hv) * V + r0 + rl;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            vw[i] = vb[static_cast<size_t>(i < T ? i : T - 1) * HV * V];
-    }
-    float dpre[kDPre];
-    load_deltas(p.rd + head * L * V + r0, V, L, base, hist, lane, dpre);
+    // the checkpoint rows, behind the key side's loads: loads complete in
+    // order for the wait counter, so waiting for the key side does not wait
+    // for these
+    f32x4 sraw[K / 16];
+    load_tile<K>(p.S + (head * V + r0) * K, lane, sraw);
 
     // ---- 2. dot products of this wave's key rows and the window columns;
     // norms; X (one wave); gates and prefix sums (another)
@@ -645,11 +643,17 @@ __global__ __launch_bounds__(kDcThreads, MINW) void dcache_verify_kernel(const D
             }
         }
     }
-    // the checkpoint rows, issued once the key operands' registers are free:
-    // their latency overlaps the coefficient phase, and the lower register
-    // peak lets more workgroups share a compute unit
-    f32x4 sraw[K / 16];
-    load_tile<K>(p.S + (head * V + r0) * K, lane, sraw);
+    // the stored deltas and window values, issued once the key operands'
+    // registers are free (they are first read after the checkpoint products)
+    float dpre[kDPre];
+    load_deltas(p.rd + head * L * V + r0, V, L, base, hist, lane, dpre);
+    st vw[TM];
+    {
+        const st* vb = static_cast<const st*>(p.v) + (static_cast<size_t>(b) * T * HV + hv) * V + r0 + rl;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            vw[i] = vb[static_cast<size_t>(i < T ? i : T - 1) * HV * V];
+    }
     __syncthreads();
 
     // ---- 3. coefficients: column i < T of record j couples window token i to
