@@ -2,9 +2,10 @@
 //
 // Everything numeric that two kernels must reproduce bit for bit lives here
 // once: the gating of a window token, the l2 norm and the gated delta step of
-// one state row.  The ring verify and the snapshot verify both call gdn_gate,
-// so the gate/beta they record in the ring are the same bits; the exact fold
-// and the snapshot verify both call rnorm16/step_row, so folding a recorded
+// one state row (with the head's decay carried in a scalar).  The ring
+// verify and the snapshot verify both call gdn_gate, so the gate/beta they
+// record in the ring are the same bits; the exact fold and the snapshot
+// verify both call rnorm16/scale_decay/step_row, so folding a recorded
 // window reproduces the snapshot path's state exactly.
 #pragma once
 
@@ -142,22 +143,46 @@ __device__ __forceinline__ float rnorm16(const float (&x)[EPL], float eps)
     return 1.0f / sqrtf(ss + eps);
 }
 
-// S_row <- e^g S_row; u = S_row . k_hat; S_row += beta (v - u) k_hat
+// The state of one (slot, value head) is carried as c S': one scalar c
+// shared by all its rows, and the rows S'.  A record's decay e^g multiplies c
+// only; the rows take the delta-rule step divided through by c, so a step
+// costs no per-element decay.  When c would drop below 2^-64 the rows absorb
+// it (S' <- c S', c <- 1), which keeps S' within 2^64 of the state.  The
+// gates are at most 1 (g <= 0), so c stays in [2^-64, 1].
+constexpr float kScaleFloor = 5.421010862427522e-20f;   // 2^-64
+
+// c <- c e^g.  True when the rows must first be multiplied by f (and c is
+// then 1).
+__device__ __forceinline__ bool scale_decay(float& c, float decay, float& f)
+{
+    f = c * decay;
+    const bool absorb = f < kScaleFloor;
+    c = absorb ? 1.0f : f;
+    return absorb;
+}
+
+// One record on a row held as S' (state c S'): u' = S' . k_hat, then
+// S' += (bc v - beta u') k_hat with bc = beta / c, i.e. the delta rule
+// S <- S + beta (v - c u') k_hat divided by c.
 template <int EPL>
 __device__ __forceinline__ void step_row(float (&s)[EPL], const float (&kh)[EPL], float v,
-                                         float decay, float beta)
+                                         float bc, float beta)
 {
     float u = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        s[e] = s[e] * decay;
+    for (int e = 0; e < EPL; ++e)
         u = __builtin_fmaf(s[e], kh[e], u);
-    }
     u = group16_sum(u);
-    const float d = beta * (v - u);
+    const float d = __builtin_fmaf(-beta, u, bc * v);
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         s[e] = __builtin_fmaf(d, kh[e], s[e]);
+}
+
+// beta / c for step_row
+__device__ __forceinline__ float scaled_beta(float beta, float c)
+{
+    return beta * __builtin_amdgcn_rcpf(c);
 }
 
 __device__ __forceinline__ int clamp_wp(int wp, int L, int T)

@@ -12,8 +12,9 @@
 // 64*m + 4*c + e.  State loads/stores are 256-byte contiguous per row and
 // per instruction; the row dot products reduce over 16 lanes with DPP.  Both
 // recurrence kernels run the identical per-record arithmetic (rnorm16,
-// step_row from gdn_common.h), which is what makes the fold of a recorded
-// window bit-identical to the snapshot of the same window.
+// scale_decay, step_row from gdn_common.h: the head's decay is carried in a
+// scalar, not applied to every element), which is what makes the fold of a
+// recorded window bit-identical to the snapshot of the same window.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -243,6 +244,7 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
     prep(0, min(RB, n));
     __syncthreads();
 
+    float cs = 1.0f;      // the state is cs S' (step_row)
     const int nbatch = (n + RB - 1) / RB;
     for (int bi = 0; bi < nbatch; ++bi) {
         const int buf = bi & 1;
@@ -254,9 +256,18 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
             float kh[EPL];
             load_cols_f32<K>(sh.khs[buf][jj], c, kh);
             const float dec = gbuf[buf][jj], bta = bbuf[buf][jj];
+            float f;
+            if (scale_decay(cs, dec, f)) {
+#pragma unroll
+                for (int j = 0; j < RPG; ++j)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e)
+                        sv[j][e] *= f;
+            }
+            const float bc = scaled_beta(bta, cs);
 #pragma unroll
             for (int j = 0; j < RPG; ++j)
-                step_row<EPL>(sv[j], kh, Act::load(vb + jj * TR + 16 * j + row16), dec, bta);
+                step_row<EPL>(sv[j], kh, Act::load(vb + jj * TR + 16 * j + row16), bc, bta);
         }
         // buffer buf ^ 1 was last read by the previous batch's steps, which
         // every thread finished before the barrier that ended that batch
@@ -268,8 +279,12 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
     }
 
 #pragma unroll
-    for (int j = 0; j < RPG; ++j)
+    for (int j = 0; j < RPG; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            sv[j][e] = cs * sv[j][e];
         store_cols_f32<K>(Srow + static_cast<size_t>(16 * j) * K, c, sv[j]);
+    }
 }
 
 // Persistent fold: every workgroup compacts the rows to fold (in chunks of
@@ -421,19 +436,26 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
     }
     __syncthreads();
 
+    float cs = 1.0f;      // the state is cs S' (step_row)
     for (int t = 0; t < T; ++t) {
         const size_t tok = tok0 + t;
         float kh[EPL], qh[EPL];
         load_cols_f32<K>(khs[t], c, kh);
         load_cols_f32<K>(qhs[t], c, qh);
         const float vc = Act::load(vst + t * 16 + row16);
-        step_row<EPL>(sv, kh, vc, gs[t], bs[t]);
+        float f;
+        if (scale_decay(cs, gs[t], f)) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                sv[e] *= f;
+        }
+        step_row<EPL>(sv, kh, vc, scaled_beta(bs[t], cs), bs[t]);
 
         float* srow = p.snap + (((static_cast<size_t>(b) * T + t) * p.HV + hv) * p.V + vrow) * K;
 #pragma unroll
         for (int m = 0; m < K / 64; ++m)
             *reinterpret_cast<f32x4*>(srow + 64 * m + 4 * c) =
-                f32x4{sv[4 * m], sv[4 * m + 1], sv[4 * m + 2], sv[4 * m + 3]};
+                f32x4{cs * sv[4 * m], cs * sv[4 * m + 1], cs * sv[4 * m + 2], cs * sv[4 * m + 3]};
 
         float dot = 0.0f;
 #pragma unroll
@@ -441,7 +463,7 @@ __global__ __launch_bounds__(256) void snapshot_kernel(const RecParams p)
             dot = __builtin_fmaf(sv[e], qh[e], dot);
         dot = group16_sum(dot);
         if (c == 0)
-            static_cast<st*>(p.o)[(tok * p.HV + hv) * p.V + vrow] = Act::from_f32(p.scale * dot);
+            static_cast<st*>(p.o)[(tok * p.HV + hv) * p.V + vrow] = Act::from_f32(p.scale * (cs * dot));
 
         if (p.write_ring) {
             const int ph = (base + wpc + t) & (L - 1);
