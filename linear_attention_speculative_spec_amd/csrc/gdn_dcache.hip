@@ -293,28 +293,6 @@ __device__ __forceinline__ float raw_sumsq(const RawChunk<Act>& r, float ss)
     return ss;
 }
 
-// The chunk's eight values as fp32 (exact for bf16; hi + lo for fp32).
-template <class Act>
-__device__ __forceinline__ void chunk_values(const KeyChunk<Act>& c, float (&x)[8])
-{
-    const uint4 h = __builtin_bit_cast(uint4, c.hi);
-    const uint32_t u[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(u[e] << 16);
-        x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-    }
-    if constexpr (Act::bytes == 4) {
-        const uint4 w = __builtin_bit_cast(uint4, c.lo);
-        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[2 * e] += __uint_as_float(v[e] << 16);
-            x[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
-        }
-    }
-}
-
 template <class Act>
 __device__ __forceinline__ f32x4 key_product(const KeyChunk<Act>& a, const KeyChunk<Act>& b, f32x4 acc)
 {
@@ -324,15 +302,6 @@ __device__ __forceinline__ f32x4 key_product(const KeyChunk<Act>& a, const KeyCh
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
     }
     return acc;
-}
-
-// The chunk's raw bits to the ring (its bit-exact record).
-template <class Act>
-__device__ __forceinline__ void store_raw(typename Act::storage* dst, const RawChunk<Act>& c)
-{
-    *reinterpret_cast<uint4*>(dst) = c.w[0];
-    if constexpr (Act::bytes == 4)
-        *reinterpret_cast<uint4*>(dst + 4) = c.w[1];
 }
 
 // Checkpoint rows r0 .. r0 + 15 of one (slot, value head): load i of lane l
