@@ -242,6 +242,15 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
         load_cols_f32<K>(Srow + static_cast<size_t>(16 * j) * K, c, sv[j]);
     commit(0);
     prep(0, min(RB, n));
+    // The state rows' loads complete here (a use of each row register), so
+    // the record loop carries no wait for them: placed there, such a wait
+    // would also hold up, at the first record of every batch, the prefetch
+    // of the next batch issued after the state's loads.
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            asm volatile("" ::"v"(sv[j][e]));
     __syncthreads();
 
     float cs = 1.0f;      // the state is cs S' (step_row)
