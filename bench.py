@@ -169,6 +169,71 @@ def traffic_from_profile():
     return float(m_bytes.group(1))
 
 
+def interleaved_verifies(args, sh, gs, gv, params, slots, cd, w, bf, f32, i32, rounds=8, calls=20):
+    """Median launch time of the raw-replay verify and of the d-cache verify,
+    timed in alternating blocks on identical state (rings of both designs
+    filled with the same records by one-token verifies).  The first two
+    rounds are dropped (clocks settling)."""
+    import torch
+    dev = "cuda:0"
+    n_hist = int(cd.write_pos[slots].max())
+    hw = synth_history(sh, args.seed + 1, n_hist)
+    A_log, dt_bias = f32(params.A_log), f32(params.dt_bias)
+
+    def rings():
+        return [torch.zeros(sh.num_slots, sh.H, sh.L, sh.K, dtype=torch.bfloat16, device=dev),
+                torch.zeros(sh.num_slots, sh.HV, sh.L, sh.V, dtype=torch.bfloat16, device=dev),
+                torch.zeros(sh.num_slots, sh.HV, sh.L, dtype=torch.float32, device=dev),
+                torch.zeros(sh.num_slots, sh.HV, sh.L, dtype=torch.float32, device=dev)]
+
+    Sr, Sd = f32(params.S0), f32(params.S0)
+    rr, rd4 = rings(), rings()
+    rd = torch.zeros(sh.num_slots, sh.HV, sh.L, sh.V, dtype=torch.float32, device=dev)
+    dslots = i32(slots)
+    gs1 = gs.replace(T=1)
+    scratch = torch.empty(sh.B, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    zeros = i32(np.zeros(sh.num_slots))
+    base = i32(cd.cache_base)
+    for r, x in enumerate(hw):
+        sl = i32(np.where(cd.write_pos[slots] > r, slots, -1).astype(np.int32))
+        xw = [bf(y) for y in (x.q, x.k, x.v, x.a, x.b)]
+        wpr = i32(np.full(sh.num_slots, r))
+        gv.gdn_spec_verify_ring(gs1, *xw, A_log, dt_bias, Sr, sl, wpr, base, zeros, *rr, 1, 0, scratch)
+        gv.gdn_spec_verify_dcache(gs1, *xw, A_log, dt_bias, Sd, sl, wpr, base, zeros, *rd4, rd, 1, 0,
+                                  scratch)
+    wp0 = cd.write_pos.astype(np.int32)
+    cur = [i32(wp0), i32(cd.cache_base), i32((wp0 + 2 * sh.max_spec > sh.L).astype(np.int32))]
+    o = torch.empty(sh.B * sh.T, sh.HV, sh.V, dtype=torch.bfloat16, device=dev)
+    fns = {"raw": lambda: gv.gdn_spec_verify_ring(gs, *w, A_log, dt_bias, Sr, dslots, *cur, *rr, 1, 0, o),
+           "dcache": lambda: gv.gdn_spec_verify_dcache(gs, *w, A_log, dt_bias, Sd, dslots, *cur, *rd4,
+                                                       rd, 1, 0, o)}
+    res = {k: [] for k in fns}
+    for _ in range(rounds + 2):
+        for k, fn in fns.items():
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(calls)]
+            for e0, e1 in evs:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            res[k].append(float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3))
+    del Sr, Sd, rr, rd4, rd
+    return {"rounds": rounds, "calls_per_round": calls,
+            "raw_verify_us": float(np.median(res["raw"][2:])),
+            "dcache_verify_us": float(np.median(res["dcache"][2:])),
+            "raw_rounds_us": [round(x, 1) for x in res["raw"][2:]],
+            "dcache_rounds_us": [round(x, 1) for x in res["dcache"][2:]]}
+
+
+def synth_history(sh, seed, n):
+    from linear_attention_speculative_spec_amd import synth
+    return synth.history_windows(synth.make_rng(seed), sh, n)
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -489,6 +554,15 @@ def main():
         log(f"[bench] d-cache: step {d_step:.1f} us, verify {d_ver:.1f} us "
             f"({dbytes / (d_ver * 1e-6) / 1e9:.0f} GB/s)")
         del rkd, rvd, rgd, rbd, rdd, Sd
+
+        # The two verifies on equal terms: fresh rings of both designs filled
+        # with the same records, the same checkpoint, cursors and window,
+        # timed in alternating blocks in this one process (the legs above run
+        # one after the other, at different points of the run).
+        result["dcache"]["interleaved"] = interleaved_verifies(args, sh, gs, gv, params, slots, cd,
+                                                               wins[0], bf, f32, i32)
+        log(f"[bench] interleaved: raw replay {result['dcache']['interleaved']['raw_verify_us']:.1f} us, "
+            f"d-cache {result['dcache']['interleaved']['dcache_verify_us']:.1f} us")
 
     if not args.no_kda:
         traj = [int(hist_per_step[i].sum() + fold_per_step[i].sum()) for i in range(n_steps)]
