@@ -555,10 +555,10 @@ def main():
             f"({dbytes / (d_ver * 1e-6) / 1e9:.0f} GB/s)")
         del rkd, rvd, rgd, rbd, rdd, Sd
 
-        # The two verifies on equal terms: fresh rings of both designs filled
-        # with the same records, the same checkpoint, cursors and window,
-        # timed in alternating blocks in this one process (the legs above run
-        # one after the other, at different points of the run).
+        # The two verifies on a fixed state: fresh rings of both designs
+        # filled with the same records, the same checkpoint, cursors and
+        # window, timed in alternating blocks of repeated calls in this one
+        # process (the trajectory legs above step each design on its own).
         result["dcache"]["interleaved"] = interleaved_verifies(args, sh, gs, gv, params, slots, cd,
                                                                wins[0], bf, f32, i32)
         log(f"[bench] interleaved: raw replay {result['dcache']['interleaved']['raw_verify_us']:.1f} us, "
