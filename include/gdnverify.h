@@ -202,7 +202,9 @@ size_t gdn_dring_bytes(const gdn_shape *shape);
  * The step reads rawk/rawv/g/beta exactly as recorded, normalises the key
  * with l2norm_eps and uses the same arithmetic as gdn_recurrent_verify_snapshot,
  * so folding a ring written by a verify reproduces the snapshot path's state
- * bit for bit.  Cursors are not modified: a row folded while unflagged must
+ * bit for bit.  (Both carry a head's decay in one scalar instead of
+ * multiplying every state element by e^g at every record: the same step in
+ * exact arithmetic, rounded differently from the plain form.)  Cursors are not modified: a row folded while unflagged must
  * have its cursors rebased (e.g. gdn_reset_cursors) before its next verify.
  * num_layers >= 1 folds that many layers in one launch (out-of-forward work,
  * so the layer axis is parallel: PR #33102 report, the all-layer commit
