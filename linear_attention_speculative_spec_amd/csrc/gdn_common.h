@@ -5,8 +5,9 @@
 // one state row (with the head's decay carried in a scalar).  The ring
 // verify and the snapshot verify both call gdn_gate, so the gate/beta they
 // record in the ring are the same bits; the exact fold and the snapshot
-// verify both call rnorm16/scale_decay/step_row, so folding a recorded
-// window reproduces the snapshot path's state exactly.
+// verify both call rnorm16/scale_decay/step_row (or step_rows4, which gives
+// four rows step_row's bits), so folding a recorded window reproduces the
+// snapshot path's state exactly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -177,6 +178,51 @@ __device__ __forceinline__ void step_row(float (&s)[EPL], const float (&kh)[EPL]
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         s[e] = __builtin_fmaf(d, kh[e], s[e]);
+}
+
+// step_row on four rows held by one 16-lane group, with the same bits for
+// each row.  The four dot products are reduced transposed: at every stage a
+// lane adds, for fewer rows, exactly the two partial sums that group16_sum
+// adds for each row (quad_perm pairs, then the other quad of the octet, then
+// the other octet; fp add is commutative, so the operand order per lane does
+// not matter).  After the first two stages lane i holds row 2 (i & 1) +
+// ((i >> 1) & 1); the two rotations leave the full sums in quads 1 and 3
+// (quads 0 and 2 add the octets in another association and are not used).
+// One d per lane, then the four d are broadcast from lanes 12..15, and every
+// lane updates all four rows.  v points at row 0's value; row j's is
+// v[16 j].  vofs = 16 * (lane's row).
+template <class Act, int EPL>
+__device__ __forceinline__ void step_rows4(float (&s)[4][EPL], const float (&kh)[EPL],
+                                           const typename Act::storage* v, int vofs, bool odd,
+                                           bool second, float bc, float beta)
+{
+    float u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u[j] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            u[j] = __builtin_fmaf(s[j][e], kh[e], u[j]);
+    }
+    // lanes i, i^1: even lanes keep rows 0 and 1, odd lanes rows 2 and 3
+    const float ka = odd ? u[2] : u[0], kb = odd ? u[3] : u[1];
+    const float sa = odd ? u[0] : u[2], sb = odd ? u[1] : u[3];
+    const float y0 = ka + dpp<0xB1>(sa), y1 = kb + dpp<0xB1>(sb);
+    // lanes i, i^2 (same parity): bit 1 picks the row
+    const float k2 = second ? y1 : y0, s2 = second ? y0 : y1;
+    float z = k2 + dpp<0x4E>(s2);
+    z += dpp<0x124>(z);   // row_ror:4: quad q adds quad q-1
+    z += dpp<0x128>(z);   // row_ror:8: quad q adds quad q-2
+    const float d = __builtin_fmaf(-beta, z, bc * Act::load(v + vofs));
+    // row j's d is on lane 12 + (j >> 1) + 2 (j & 1) of the group
+    const float d0 = dpp<0x15C>(d), d1 = dpp<0x15E>(d), d2 = dpp<0x15D>(d), d3 = dpp<0x15F>(d);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        s[0][e] = __builtin_fmaf(d0, kh[e], s[0][e]);
+        s[1][e] = __builtin_fmaf(d1, kh[e], s[1][e]);
+        s[2][e] = __builtin_fmaf(d2, kh[e], s[2][e]);
+        s[3][e] = __builtin_fmaf(d3, kh[e], s[3][e]);
+    }
 }
 
 // beta / c for step_row

@@ -12,9 +12,10 @@
 // 64*m + 4*c + e.  State loads/stores are 256-byte contiguous per row and
 // per instruction; the row dot products reduce over 16 lanes with DPP.  Both
 // recurrence kernels run the identical per-record arithmetic (rnorm16,
-// scale_decay, step_row from gdn_common.h: the head's decay is carried in a
-// scalar, not applied to every element), which is what makes the fold of a
-// recorded window bit-identical to the snapshot of the same window.
+// scale_decay, step_row from gdn_common.h, or step_rows4 where a lane group
+// holds four rows, which gives each row step_row's bits: the head's decay is
+// carried in a scalar, not applied to every element), which is what makes the
+// fold of a recorded window bit-identical to the snapshot of the same window.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -254,6 +255,9 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
     __syncthreads();
 
     float cs = 1.0f;      // the state is cs S' (step_row)
+    // step_rows4: the row whose d this lane forms
+    const bool odd = (c & 1) != 0, second = (c & 2) != 0;
+    const int vofs = 16 * (2 * (c & 1) + ((c >> 1) & 1));
     const int nbatch = (n + RB - 1) / RB;
     for (int bi = 0; bi < nbatch; ++bi) {
         const int buf = bi & 1;
@@ -274,9 +278,13 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
                         sv[j][e] *= f;
             }
             const float bc = scaled_beta(bta, cs);
+            if constexpr (RPG == 4) {
+                step_rows4<Act, EPL>(sv, kh, vb + jj * TR + row16, vofs, odd, second, bc, bta);
+            } else {
 #pragma unroll
-            for (int j = 0; j < RPG; ++j)
-                step_row<EPL>(sv[j], kh, Act::load(vb + jj * TR + 16 * j + row16), bc, bta);
+                for (int j = 0; j < RPG; ++j)
+                    step_row<EPL>(sv[j], kh, Act::load(vb + jj * TR + 16 * j + row16), bc, bta);
+            }
         }
         // buffer buf ^ 1 was last read by the previous batch's steps, which
         // every thread finished before the barrier that ended that batch
