@@ -180,17 +180,45 @@ __device__ __forceinline__ void step_row(float (&s)[EPL], const float (&kh)[EPL]
         s[e] = __builtin_fmaf(d, kh[e], s[e]);
 }
 
+// group16_sum of four values (one per state row of the lane group) reduced
+// transposed, with the same bits per row: at every stage a lane adds, for
+// fewer rows, exactly the two partial sums that group16_sum adds (quad_perm
+// pairs, then the other quad of the octet, then the other octet; fp add is
+// commutative, so the operand order per lane does not matter).  After the
+// first two stages lane i holds row 2 (i & 1) + ((i >> 1) & 1) (odd = i & 1,
+// second = i & 2); the two rotations leave the full sums in quads 1 and 3
+// (quads 0 and 2 add the octets in another association).  Row j's sum is
+// then on lane 12 + (j >> 1) + 2 (j & 1) of the group: bcast_row<j> reads it.
+__device__ __forceinline__ float sum16_rows4(const float (&u)[4], bool odd, bool second)
+{
+    // lanes i, i^1: even lanes keep rows 0 and 1, odd lanes rows 2 and 3
+    const float ka = odd ? u[2] : u[0], kb = odd ? u[3] : u[1];
+    const float sa = odd ? u[0] : u[2], sb = odd ? u[1] : u[3];
+    const float y0 = ka + dpp<0xB1>(sa), y1 = kb + dpp<0xB1>(sb);
+    // lanes i, i^2 (same parity): bit 1 picks the row
+    const float k2 = second ? y1 : y0, s2 = second ? y0 : y1;
+    float z = k2 + dpp<0x4E>(s2);
+    z += dpp<0x124>(z);   // row_ror:4: quad q adds quad q-1
+    z += dpp<0x128>(z);   // row_ror:8: quad q adds quad q-2
+    return z;
+}
+
+// Row j's value of a per-lane quantity laid out as sum16_rows4 leaves it,
+// on every lane of the group (row_newbcast from lane 12 + (j >> 1) + 2 (j & 1)).
+template <int J>
+__device__ __forceinline__ float bcast_row(float x)
+{
+    return dpp<0x15C + (J >> 1) + 2 * (J & 1)>(x);
+}
+
+// Lane-invariant parts of the transposed layout: the lane's row is
+// 2 odd + second.
+__device__ __forceinline__ int row4_of_lane(int c) { return 2 * (c & 1) + ((c >> 1) & 1); }
+
 // step_row on four rows held by one 16-lane group, with the same bits for
-// each row.  The four dot products are reduced transposed: at every stage a
-// lane adds, for fewer rows, exactly the two partial sums that group16_sum
-// adds for each row (quad_perm pairs, then the other quad of the octet, then
-// the other octet; fp add is commutative, so the operand order per lane does
-// not matter).  After the first two stages lane i holds row 2 (i & 1) +
-// ((i >> 1) & 1); the two rotations leave the full sums in quads 1 and 3
-// (quads 0 and 2 add the octets in another association and are not used).
-// One d per lane, then the four d are broadcast from lanes 12..15, and every
-// lane updates all four rows.  v points at row 0's value; row j's is
-// v[16 j].  vofs = 16 * (lane's row).
+// each row: the dot products are reduced by sum16_rows4, each lane forms its
+// own row's d, and the four d are broadcast to the group.  v points at row
+// 0's value; row j's is v[16 j].  vofs = 16 * row4_of_lane(lane & 15).
 template <class Act, int EPL>
 __device__ __forceinline__ void step_rows4(float (&s)[4][EPL], const float (&kh)[EPL],
                                            const typename Act::storage* v, int vofs, bool odd,
@@ -204,18 +232,9 @@ __device__ __forceinline__ void step_rows4(float (&s)[4][EPL], const float (&kh)
         for (int e = 0; e < EPL; ++e)
             u[j] = __builtin_fmaf(s[j][e], kh[e], u[j]);
     }
-    // lanes i, i^1: even lanes keep rows 0 and 1, odd lanes rows 2 and 3
-    const float ka = odd ? u[2] : u[0], kb = odd ? u[3] : u[1];
-    const float sa = odd ? u[0] : u[2], sb = odd ? u[1] : u[3];
-    const float y0 = ka + dpp<0xB1>(sa), y1 = kb + dpp<0xB1>(sb);
-    // lanes i, i^2 (same parity): bit 1 picks the row
-    const float k2 = second ? y1 : y0, s2 = second ? y0 : y1;
-    float z = k2 + dpp<0x4E>(s2);
-    z += dpp<0x124>(z);   // row_ror:4: quad q adds quad q-1
-    z += dpp<0x128>(z);   // row_ror:8: quad q adds quad q-2
+    const float z = sum16_rows4(u, odd, second);
     const float d = __builtin_fmaf(-beta, z, bc * Act::load(v + vofs));
-    // row j's d is on lane 12 + (j >> 1) + 2 (j & 1) of the group
-    const float d0 = dpp<0x15C>(d), d1 = dpp<0x15E>(d), d2 = dpp<0x15D>(d), d3 = dpp<0x15F>(d);
+    const float d0 = bcast_row<0>(d), d1 = bcast_row<1>(d), d2 = bcast_row<2>(d), d3 = bcast_row<3>(d);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         s[0][e] = __builtin_fmaf(d0, kh[e], s[0][e]);

@@ -163,6 +163,9 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, grp = lane >> 4;
     const int row16 = w * 4 + grp;
+    static_assert(kKdaRPG == 4, "the record loop reduces four rows per lane group");
+    const bool odd = (c & 1) != 0, second = (c & 2) != 0;
+    const int vofs = 16 * row4_of_lane(c);     // the row whose d pair this lane forms
     const int h = hv / (p.HV / p.H);
     const int L = p.L;
     const size_t recs = static_cast<size_t>(layer) * static_cast<size_t>(p.lsR) * L;   // ring records before the layer
@@ -315,23 +318,28 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             cols_f32<K>(sh.pair_vec(pp, 1), c, a1);
             const float cj = sh.cbuf[pp];
             const float b0 = sh.bbuf[2 * pp], b1 = sh.bbuf[2 * pp + 1];
-            float d0[kKdaRPG], d1[kKdaRPG];
+            // the four rows' sums reduced transposed (sum16_rows4: each row
+            // gets group16_sum's bits); each lane forms its own row's d pair
+            float u0[kKdaRPG], u1[kKdaRPG];
 #pragma unroll
             for (int r = 0; r < kKdaRPG; ++r) {
-                float u0 = 0.0f, u1 = 0.0f;
+                u0[r] = 0.0f;
+                u1[r] = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
-                    u0 = __builtin_fmaf(sv[r][e], a0[e], u0);
-                    u1 = __builtin_fmaf(sv[r][e], a1[e], u1);
+                    u0[r] = __builtin_fmaf(sv[r][e], a0[e], u0[r]);
+                    u1[r] = __builtin_fmaf(sv[r][e], a1[e], u1[r]);
                 }
-                u0 = group16_sum(u0);
-                u1 = group16_sum(u1);
-                const float bv0 = sh.bvf[(2 * pp) * TR + 16 * r + row16];
-                const float bv1 = sh.bvf[(2 * pp + 1) * TR + 16 * r + row16];
-                d0[r] = __builtin_fmaf(-b0, u0, bv0);
-                u1 = __builtin_fmaf(d0[r], cj, u1);
-                d1[r] = __builtin_fmaf(-b1, u1, bv1);
             }
+            const float z0 = sum16_rows4(u0, odd, second);
+            float z1 = sum16_rows4(u1, odd, second);
+            const float bv0 = sh.bvf[(2 * pp) * TR + vofs + row16];
+            const float bv1 = sh.bvf[(2 * pp + 1) * TR + vofs + row16];
+            const float e0 = __builtin_fmaf(-b0, z0, bv0);
+            z1 = __builtin_fmaf(e0, cj, z1);
+            const float e1 = __builtin_fmaf(-b1, z1, bv1);
+            const float d0[kKdaRPG] = {bcast_row<0>(e0), bcast_row<1>(e0), bcast_row<2>(e0), bcast_row<3>(e0)};
+            const float d1[kKdaRPG] = {bcast_row<0>(e1), bcast_row<1>(e1), bcast_row<2>(e1), bcast_row<3>(e1)};
             float dd[EPL], kd[EPL], k1[EPL];
             cols_f32<K>(sh.pair_vec(pp, 2), c, dd);
             cols_f32<K>(sh.pair_vec(pp, 3), c, kd);

@@ -257,7 +257,7 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
     float cs = 1.0f;      // the state is cs S' (step_row)
     // step_rows4: the row whose d this lane forms
     const bool odd = (c & 1) != 0, second = (c & 2) != 0;
-    const int vofs = 16 * (2 * (c & 1) + ((c >> 1) & 1));
+    const int vofs = 16 * row4_of_lane(c);
     const int nbatch = (n + RB - 1) / RB;
     for (int bi = 0; bi < nbatch; ++bi) {
         const int buf = bi & 1;
