@@ -59,6 +59,9 @@ def parse():
                     help="skip the per-channel-gate (KDA) layer leg")
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the 48-layer whole-stack leg")
+    ap.add_argument("--no-interleaved", action="store_true",
+                    help="skip the raw-replay / d-cache comparison on fixed state that follows "
+                         "the d-cache leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -559,10 +562,11 @@ def main():
         # filled with the same records, the same checkpoint, cursors and
         # window, timed in alternating blocks of repeated calls in this one
         # process (the trajectory legs above step each design on its own).
-        result["dcache"]["interleaved"] = interleaved_verifies(args, sh, gs, gv, params, slots, cd,
-                                                               wins[0], bf, f32, i32)
-        log(f"[bench] interleaved: raw replay {result['dcache']['interleaved']['raw_verify_us']:.1f} us, "
-            f"d-cache {result['dcache']['interleaved']['dcache_verify_us']:.1f} us")
+        if not args.no_interleaved:
+            result["dcache"]["interleaved"] = interleaved_verifies(args, sh, gs, gv, params, slots, cd,
+                                                                   wins[0], bf, f32, i32)
+            log(f"[bench] interleaved: raw replay {result['dcache']['interleaved']['raw_verify_us']:.1f} us, "
+                f"d-cache {result['dcache']['interleaved']['dcache_verify_us']:.1f} us")
 
     if not args.no_kda:
         traj = [int(hist_per_step[i].sum() + fold_per_step[i].sum()) for i in range(n_steps)]
@@ -973,7 +977,7 @@ def summarize_kda_profile(d):
 
 DCACHE_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "dcache_verify_kernel_qwen3next_b256.md")
 DCACHE_SRC = os.path.join(ROOT, "linear_attention_speculative_spec_amd", "csrc", "gdn_dcache.hip")
-_DC_LEG = "--no-cpu-baseline --no-snapshot --no-fold-every-commit --no-kda --no-chain --copy-calibration"
+_DC_LEG = "--no-cpu-baseline --no-snapshot --no-fold-every-commit --no-kda --no-chain --no-interleaved --copy-calibration"
 DCACHE_PROFILE_CMDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/dcprof/kt -o run --output-format csv -- "
