@@ -7,9 +7,10 @@
 //     (PR #36821 summary: a [K,V] fp32 snapshot per head-step);
 //   * the snapshot path's commit copy.
 //
-// Layout: a workgroup of 4 waves owns 16 consecutive rows of one (slot, value
-// head) state; each row lives on 16 lanes, lane c holding columns
-// 64*m + 4*c + e.  State loads/stores are 256-byte contiguous per row and
+// Layout: a workgroup of 4 waves owns a tile of 16 RPG rows of one (slot,
+// value head) state (the snapshot verify: RPG = 1; the fold: RPG = 4 where
+// the value rows allow 64-row tiles); each row lives on 16 lanes, lane c
+// holding columns 64*m + 4*c + e.  State loads/stores are 256-byte contiguous per row and
 // per instruction; the row dot products reduce over 16 lanes with DPP.  Both
 // recurrence kernels run the identical per-record arithmetic (rnorm16,
 // scale_decay, step_row from gdn_common.h, or step_rows4 where a lane group
