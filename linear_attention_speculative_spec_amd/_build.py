@@ -24,6 +24,15 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The fold's four-row step updates the state on the
+# matrix units; with its accumulators in accumulation registers every record
+# would copy 32 of them back for the next dot products, so that source keeps
+# matrix-instruction operands and results in ordinary vector registers.
+EXTRA_FLAGS = {
+    "gdn_recurrence.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,7 +48,8 @@ def build_library(jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+        cmd = [cc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -216,32 +216,40 @@ __device__ __forceinline__ float bcast_row(float x)
 __device__ __forceinline__ int row4_of_lane(int c) { return 2 * (c & 1) + ((c >> 1) & 1); }
 
 // step_row on four rows held by one 16-lane group, with the same bits for
-// each row: the dot products are reduced by sum16_rows4, each lane forms its
-// own row's d, and the four d are broadcast to the group.  v points at row
-// 0's value; row j's is v[16 j].  vofs = 16 * row4_of_lane(lane & 15).
+// each row.  The lane's EPL columns of the four rows are held as a[e], one
+// 4-vector per column, register i holding row pi(i), pi = (0, 2, 1, 3): the
+// row whose d lane i of each quad forms.  The dot products run on the vector
+// ALU in step_row's order and are reduced by sum16_rows4; each lane forms its
+// own row's d.  Quads 1 and 3 hold the full sums, and quads 0 and 2 take
+// theirs by one row rotation written to banks 0 and 2 only.  The update
+// a[e] += d kh[e] is then one 4x4x1 fp32 matrix product per column (16 blocks
+// of 4 lanes; A from lane i of a block is the d of register i's row, B from
+// each lane is its own column's key): one product and one add per element,
+// rounded once, so each element gets step_row's fmaf bits.
+// vofs = 16 * row4_of_lane(lane & 15); v points at row 0's value (row j's is
+// v[16 j]).
 template <class Act, int EPL>
-__device__ __forceinline__ void step_rows4(float (&s)[4][EPL], const float (&kh)[EPL],
+__device__ __forceinline__ void step_rows4(f32x4 (&a)[EPL], const float (&kh)[EPL],
                                            const typename Act::storage* v, int vofs, bool odd,
                                            bool second, float bc, float beta)
 {
-    float u[4];
+    float ur[4];   // by register
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u[j] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        ur[i] = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            u[j] = __builtin_fmaf(s[j][e], kh[e], u[j]);
+            ur[i] = __builtin_fmaf(a[e][i], kh[e], ur[i]);
     }
+    const float u[4] = {ur[0], ur[2], ur[1], ur[3]};   // by row
     const float z = sum16_rows4(u, odd, second);
     const float d = __builtin_fmaf(-beta, z, bc * Act::load(v + vofs));
-    const float d0 = bcast_row<0>(d), d1 = bcast_row<1>(d), d2 = bcast_row<2>(d), d3 = bcast_row<3>(d);
+    // row_ror:4 into banks 0 and 2: quad 0 reads quad 3, quad 2 reads quad 1
+    const float dm = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, d), __builtin_bit_cast(int, d), 0x124, 0xF, 0x5, false));
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        s[0][e] = __builtin_fmaf(d0, kh[e], s[0][e]);
-        s[1][e] = __builtin_fmaf(d1, kh[e], s[1][e]);
-        s[2][e] = __builtin_fmaf(d2, kh[e], s[2][e]);
-        s[3][e] = __builtin_fmaf(d3, kh[e], s[3][e]);
-    }
+    for (int e = 0; e < EPL; ++e)
+        a[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(dm, kh[e], a[e], 0, 0, 0);
 }
 
 // beta / c for step_row

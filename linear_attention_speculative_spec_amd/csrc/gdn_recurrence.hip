@@ -14,7 +14,8 @@
 // per instruction; the row dot products reduce over 16 lanes with DPP.  Both
 // recurrence kernels run the identical per-record arithmetic (rnorm16,
 // scale_decay, step_row from gdn_common.h, or step_rows4 where a lane group
-// holds four rows, which gives each row step_row's bits: the head's decay is
+// holds four rows and updates them on the matrix units, which gives each row
+// step_row's bits: the head's decay is
 // carried in a scalar, not applied to every element), which is what makes the
 // fold of a recorded window bit-identical to the snapshot of the same window.
 #include <type_traits>
@@ -253,6 +254,15 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             asm volatile("" ::"v"(sv[j][e]));
+    // four rows per lane group: the state per column, in step_rows4's
+    // register order (rows 0, 2, 1, 3)
+    constexpr bool kRows4 = RPG == 4;
+    f32x4 av[kRows4 ? EPL : 1];
+    if constexpr (kRows4) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            av[e] = f32x4{sv[0][e], sv[2][e], sv[1][e], sv[3][e]};
+    }
     __syncthreads();
 
     float cs = 1.0f;      // the state is cs S' (step_row)
@@ -272,15 +282,23 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
             const float dec = gbuf[buf][jj], bta = bbuf[buf][jj];
             float f;
             if (scale_decay(cs, dec, f)) {
-#pragma unroll
-                for (int j = 0; j < RPG; ++j)
+                if constexpr (kRows4) {
 #pragma unroll
                     for (int e = 0; e < EPL; ++e)
-                        sv[j][e] *= f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            av[e][i] *= f;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < RPG; ++j)
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            sv[j][e] *= f;
+                }
             }
             const float bc = scaled_beta(bta, cs);
-            if constexpr (RPG == 4) {
-                step_rows4<Act, EPL>(sv, kh, vb + jj * TR + row16, vofs, odd, second, bc, bta);
+            if constexpr (kRows4) {
+                step_rows4<Act, EPL>(av, kh, vb + jj * TR + row16, vofs, odd, second, bc, bta);
             } else {
 #pragma unroll
                 for (int j = 0; j < RPG; ++j)
@@ -296,6 +314,15 @@ __device__ void fold_item(P& p, FoldShared<Act, K, RPG>& sh, int s, int n, int b
         __syncthreads();
     }
 
+    if constexpr (kRows4) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            sv[0][e] = av[e][0];
+            sv[2][e] = av[e][1];
+            sv[1][e] = av[e][2];
+            sv[3][e] = av[e][3];
+        }
+    }
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
 #pragma unroll
