@@ -24,12 +24,14 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source additions.  The fold's four-row step updates the state on the
-# matrix units; with its accumulators in accumulation registers every record
-# would copy 32 of them back for the next dot products, so that source keeps
-# matrix-instruction operands and results in ordinary vector registers.
+# Per-source additions.  The fold's and the KDA replay's four-row steps update
+# the state on the matrix units; with their accumulators in accumulation
+# registers every record would copy 32 of them back for the next dot
+# products, so those sources keep matrix-instruction operands and results in
+# ordinary vector registers.
 EXTRA_FLAGS = {
     "gdn_recurrence.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gdn_kda.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

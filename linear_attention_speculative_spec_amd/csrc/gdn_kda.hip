@@ -150,8 +150,20 @@ __device__ __forceinline__ void act_cols(const typename Act::storage* row, int c
     }
 }
 
+// A per-lane value of the transposed four-row layout (sum16_rows4) whose
+// quads 1 and 3 are right, copied into quads 0 and 2 (row_ror:4 written to
+// banks 0 and 2 only: quad 0 reads quad 3, quad 2 reads quad 1).
+__device__ __forceinline__ float quads13(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), 0x124, 0xF, 0x5, false));
+}
+
 // Steps the tile's state rows sv through the n committed records of slot s
-// (layer `layer`, value head hv), reading the ring, in batches of 16.
+// (layer `layer`, value head hv), reading the ring, in batches of 16.  The
+// rows are held per column while the records are stepped (register i of av[e]
+// is row 0, 2, 1, 3); the two rank-1 updates of a record pair run on 4x4x1
+// fp32 matrix products, each rounded once as fmaf rounds.
 template <class Act, int K, class P>
 __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, int layer,
                            int hv, int tile, float (&sv)[kKdaRPG][K / 16])
@@ -304,6 +316,12 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             asm volatile("" ::"v"(sv[r][e]));
     if (nbatch > 0)
         commit(min(RB, n));
+    // the state per column for the matrix-unit updates, register i holding
+    // row 0, 2, 1, 3 (the row whose d lane i of each quad forms)
+    f32x4 av[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        av[e] = f32x4{sv[0][e], sv[2][e], sv[1][e], sv[3][e]};
     __syncthreads();
     // one LDS buffer: the next batch is committed after a barrier that ends
     // every thread's reads of the current one (its loads were in flight
@@ -320,17 +338,19 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             const float b0 = sh.bbuf[2 * pp], b1 = sh.bbuf[2 * pp + 1];
             // the four rows' sums reduced transposed (sum16_rows4: each row
             // gets group16_sum's bits); each lane forms its own row's d pair
-            float u0[kKdaRPG], u1[kKdaRPG];
+            float w0[4], w1[4];   // by register
 #pragma unroll
-            for (int r = 0; r < kKdaRPG; ++r) {
-                u0[r] = 0.0f;
-                u1[r] = 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                w0[i] = 0.0f;
+                w1[i] = 0.0f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
-                    u0[r] = __builtin_fmaf(sv[r][e], a0[e], u0[r]);
-                    u1[r] = __builtin_fmaf(sv[r][e], a1[e], u1[r]);
+                    w0[i] = __builtin_fmaf(av[e][i], a0[e], w0[i]);
+                    w1[i] = __builtin_fmaf(av[e][i], a1[e], w1[i]);
                 }
             }
+            const float u0[kKdaRPG] = {w0[0], w0[2], w0[1], w0[3]};
+            const float u1[kKdaRPG] = {w1[0], w1[2], w1[1], w1[3]};
             const float z0 = sum16_rows4(u0, odd, second);
             float z1 = sum16_rows4(u1, odd, second);
             const float bv0 = sh.bvf[(2 * pp) * TR + vofs + row16];
@@ -338,20 +358,20 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             const float e0 = __builtin_fmaf(-b0, z0, bv0);
             z1 = __builtin_fmaf(e0, cj, z1);
             const float e1 = __builtin_fmaf(-b1, z1, bv1);
-            const float d0[kKdaRPG] = {bcast_row<0>(e0), bcast_row<1>(e0), bcast_row<2>(e0), bcast_row<3>(e0)};
-            const float d1[kKdaRPG] = {bcast_row<0>(e1), bcast_row<1>(e1), bcast_row<2>(e1), bcast_row<3>(e1)};
+            // quads 1 and 3 hold the full sums; quads 0 and 2 take theirs
+            const float d0 = quads13(e0), d1 = quads13(e1);
             float dd[EPL], kd[EPL], k1[EPL];
             cols_f32<K>(sh.pair_vec(pp, 2), c, dd);
             cols_f32<K>(sh.pair_vec(pp, 3), c, kd);
             cols_f32<K>(sh.pair_vec(pp, 4), c, k1);
 #pragma unroll
-            for (int r = 0; r < kKdaRPG; ++r) {
+            for (int e = 0; e < EPL; ++e) {
+                f32x4 x;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    float x = sv[r][e] * dd[e];
-                    x = __builtin_fmaf(d0[r], kd[e], x);
-                    sv[r][e] = __builtin_fmaf(d1[r], k1[e], x);
-                }
+                for (int i = 0; i < 4; ++i)
+                    x[i] = av[e][i] * dd[e];
+                x = __builtin_amdgcn_mfma_f32_4x4x1f32(d0, kd[e], x, 0, 0, 0);
+                av[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(d1, k1[e], x, 0, 0, 0);
             }
         }
         if (bi + 1 < nbatch) {
@@ -359,6 +379,13 @@ __device__ void kda_replay(P& p, KdaShared<Act, K>& sh, int s, int n, int base, 
             commit(min(RB, n - (bi + 1) * RB));
         }
         __syncthreads();
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        sv[0][e] = av[e][0];
+        sv[2][e] = av[e][1];
+        sv[1][e] = av[e][2];
+        sv[3][e] = av[e][3];
     }
 }
 
