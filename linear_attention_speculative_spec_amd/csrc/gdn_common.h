@@ -215,6 +215,16 @@ __device__ __forceinline__ float bcast_row(float x)
 // 2 odd + second.
 __device__ __forceinline__ int row4_of_lane(int c) { return 2 * (c & 1) + ((c >> 1) & 1); }
 
+// A per-lane value of the sum16_rows4 layout whose quads 1 and 3 are right
+// (the full sums), copied into quads 0 and 2: row_ror:4 written to banks 0
+// and 2 only, so quad 0 reads quad 3 and quad 2 reads quad 1.  Lane i of
+// every quad then holds the value of row row4_of_lane(i).
+__device__ __forceinline__ float quads13(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), 0x124, 0xF, 0x5, false));
+}
+
 // step_row on four rows held by one 16-lane group, with the same bits for
 // each row.  The lane's EPL columns of the four rows are held as a[e], one
 // 4-vector per column, register i holding row pi(i), pi = (0, 2, 1, 3): the
@@ -244,9 +254,7 @@ __device__ __forceinline__ void step_rows4(f32x4 (&a)[EPL], const float (&kh)[EP
     const float u[4] = {ur[0], ur[2], ur[1], ur[3]};   // by row
     const float z = sum16_rows4(u, odd, second);
     const float d = __builtin_fmaf(-beta, z, bc * Act::load(v + vofs));
-    // row_ror:4 into banks 0 and 2: quad 0 reads quad 3, quad 2 reads quad 1
-    const float dm = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        __builtin_bit_cast(int, d), __builtin_bit_cast(int, d), 0x124, 0xF, 0x5, false));
+    const float dm = quads13(d);
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         a[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(dm, kh[e], a[e], 0, 0, 0);

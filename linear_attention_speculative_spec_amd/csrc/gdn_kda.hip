@@ -150,15 +150,6 @@ __device__ __forceinline__ void act_cols(const typename Act::storage* row, int c
     }
 }
 
-// A per-lane value of the transposed four-row layout (sum16_rows4) whose
-// quads 1 and 3 are right, copied into quads 0 and 2 (row_ror:4 written to
-// banks 0 and 2 only: quad 0 reads quad 3, quad 2 reads quad 1).
-__device__ __forceinline__ float quads13(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        __builtin_bit_cast(int, x), __builtin_bit_cast(int, x), 0x124, 0xF, 0x5, false));
-}
-
 // Steps the tile's state rows sv through the n committed records of slot s
 // (layer `layer`, value head hv), reading the ring, in batches of 16.  The
 // rows are held per column while the records are stepped (register i of av[e]
